@@ -1,0 +1,249 @@
+// libmoe C ABI: argument validation, workspace layout, path choice, launches.
+// Every entry point validates on the host before enqueuing anything and never
+// synchronises or reads device memory.
+#include "libmoe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <functional>
+
+#include "moe_internal.hpp"
+
+namespace {
+
+using moe::Shape;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point.  Returns MOE_OK and fills `s`.
+moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
+  if (!p) return MOE_EINVAL;
+  if (p->tokens < 0 || p->dim <= 0 || p->hidden <= 0 || p->n_experts <= 0 || p->top_k <= 0)
+    return MOE_EINVAL;
+  if (p->top_k > p->n_experts) return MOE_EINVAL;
+  if (p->dim % 8 != 0 || p->hidden % 8 != 0) return MOE_EINVAL;
+  if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return MOE_EINVAL;
+  if (p->n_experts > MOE_MAX_EXPERTS) return MOE_ENOTSUP;
+  const int64_t P = int64_t(p->tokens) * p->top_k;
+  const int64_t cap =
+      (P + int64_t(p->n_experts) * (MOE_TILE_M - 1) + MOE_TILE_M - 1) / MOE_TILE_M * MOE_TILE_M;
+  // row indices and element offsets inside one expert are int32 on the device
+  if (cap >= (int64_t(1) << 31)) return MOE_ENOTSUP;
+  if (int64_t(p->dim) * p->hidden >= (int64_t(1) << 31)) return MOE_ENOTSUP;
+  s->T = p->tokens;
+  s->D = p->dim;
+  s->H = p->hidden;
+  s->n = p->n_experts;
+  s->K = p->top_k;
+  s->cap = cap;
+  return MOE_OK;
+}
+
+// Workspace carve-up (each piece 256-byte aligned):
+//   topk_idx  int32 [T*K]     topk_gate fp32 [T*K]
+//   count     int32 [n]       offset    int32 [n+1]
+//   row_slot  int32 [cap]     slot_row  int32 [T*K]
+//   h         bf16  [cap][H]  y_rows    fp32  [cap][D]
+struct Carve {
+  size_t idx, gate, count, offset, row_slot, slot_row, h, y, total;
+};
+
+Carve carve(const Shape& s) {
+  Carve c{};
+  const size_t P = size_t(s.T) * s.K;
+  size_t o = 0;
+  c.idx = o;      o = align_up(o + P * 4, kAlign);
+  c.gate = o;     o = align_up(o + P * 4, kAlign);
+  c.count = o;    o = align_up(o + size_t(s.n) * 4, kAlign);
+  c.offset = o;   o = align_up(o + size_t(s.n + 1) * 4, kAlign);
+  c.row_slot = o; o = align_up(o + size_t(s.cap) * 4, kAlign);
+  c.slot_row = o; o = align_up(o + P * 4, kAlign);
+  c.h = o;        o = align_up(o + size_t(s.cap) * s.H * 2, kAlign);
+  c.y = o;        o = align_up(o + size_t(s.cap) * s.D * 4, kAlign);
+  c.total = o;
+  return c;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+bool use_decode(const Shape& s) { return s.T <= moe::kDecodeMaxTokens; }
+
+// `mark(i)`, when given, records stage event i (3 after the first product, 4
+// after the second).
+using MarkFn = std::function<hipError_t(int)>;
+
+moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const int32_t* offset,
+                     const int32_t* row_slot, const void* w1, const void* w3, const void* w2,
+                     float* y_rows, uint16_t* h, hipStream_t st, const MarkFn& mark = nullptr) {
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* w1b = static_cast<const uint16_t*>(w1);
+  const uint16_t* w3b = static_cast<const uint16_t*>(w3);
+  const uint16_t* w2b = static_cast<const uint16_t*>(w2);
+  hipError_t e;
+  if (use_decode(s))
+    e = moe::launch_decode_up(s, xb, count, offset, row_slot, w1b, w3b, h, st);
+  else
+    e = moe::launch_grouped_up(s, xb, offset, row_slot, w1b, w3b, h, st);
+  if (e != hipSuccess || (mark && mark(3) != hipSuccess)) return MOE_EHIP;
+  if (use_decode(s))
+    e = moe::launch_decode_down(s, count, offset, h, w2b, y_rows, st);
+  else
+    e = moe::launch_grouped_down(s, offset, h, w2b, y_rows, st);
+  if (e != hipSuccess || (mark && mark(4) != hipSuccess)) return MOE_EHIP;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity_rows(const moe_problem_t* p) {
+  Shape s;
+  if (check_problem(p, &s) != MOE_OK) return -1;
+  return s.cap;
+}
+
+size_t moe_workspace_bytes(const moe_problem_t* p) {
+  Shape s;
+  if (check_problem(p, &s) != MOE_OK) return 0;
+  return carve(s).total;
+}
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ENOTSUP: return "unsupported shape";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_decode_max_tokens(void) { return moe::kDecodeMaxTokens; }
+
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate,
+                       int32_t* topk_idx, float* topk_gate, float* logits, void* stream) {
+  Shape s;
+  moe_status_t st = check_problem(p, &s);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_gate || !topk_idx || !topk_gate) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(topk_idx) || !aligned16(topk_gate) ||
+      (logits && !aligned16(logits)))
+    return MOE_EINVAL;
+  return hip_status(moe::launch_route(s, static_cast<const uint16_t*>(x),
+                                      static_cast<const uint16_t*>(w_gate), topk_idx, topk_gate,
+                                      logits, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* expert_count,
+                         int32_t* expert_offset, int32_t* row_slot, int32_t* slot_row,
+                         void* stream) {
+  Shape s;
+  moe_status_t st = check_problem(p, &s);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  if (!topk_idx || !expert_count || !expert_offset || !row_slot || !slot_row) return MOE_EINVAL;
+  if (!aligned16(topk_idx) || !aligned16(expert_count) || !aligned16(expert_offset) ||
+      !aligned16(row_slot) || !aligned16(slot_row))
+    return MOE_EINVAL;
+  return hip_status(moe::launch_permute(s, topk_idx, expert_count, expert_offset, row_slot,
+                                        slot_row, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_t* expert_count,
+                             const int32_t* expert_offset, const int32_t* row_slot,
+                             const void* w1, const void* w3, const void* w2, float* y_rows,
+                             void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status_t st = check_problem(p, &s);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !expert_count || !expert_offset || !row_slot || !w1 || !w3 || !w2 || !y_rows)
+    return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(expert_count) || !aligned16(expert_offset) ||
+      !aligned16(row_slot) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) ||
+      !aligned16(y_rows))
+    return MOE_EINVAL;
+  const Carve c = carve(s);
+  if (!ws || ws_bytes < c.total) return MOE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_EINVAL;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  return run_ffn(s, x, expert_count, expert_offset, row_slot, w1, w3, w2, y_rows,
+                 reinterpret_cast<uint16_t*>(base + c.h), static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int32_t* slot_row,
+                         const float* topk_gate, void* out, void* stream) {
+  Shape s;
+  moe_status_t st = check_problem(p, &s);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  if (!y_rows || !slot_row || !topk_gate || !out) return MOE_EINVAL;
+  if (!aligned16(y_rows) || !aligned16(slot_row) || !aligned16(topk_gate) || !aligned16(out))
+    return MOE_EINVAL;
+  return hip_status(moe::launch_combine(s, y_rows, slot_row, topk_gate, out,
+                                        p->out_dtype == MOE_BF16,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_gate,
+                         const void* w1, const void* w3, const void* w2, void* out,
+                         int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return moe_forward_timed(p, x, w_gate, w1, w3, w2, out, topk_idx, topk_gate, ws, ws_bytes,
+                           stream, nullptr);
+}
+
+moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void* w_gate,
+                               const void* w1, const void* w3, const void* w2, void* out,
+                               int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                               void* stream, void* const* events) {
+  Shape s;
+  moe_status_t st = check_problem(p, &s);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_gate || !w1 || !w3 || !w2 || !out) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w1) || !aligned16(w3) ||
+      !aligned16(w2) || !aligned16(out) || (topk_idx && !aligned16(topk_idx)) ||
+      (topk_gate && !aligned16(topk_gate)))
+    return MOE_EINVAL;
+  const Carve c = carve(s);
+  if (!ws || ws_bytes < c.total) return MOE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_EINVAL;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(base + c.idx);
+  float* gate = topk_gate ? topk_gate : reinterpret_cast<float*>(base + c.gate);
+  int32_t* count = reinterpret_cast<int32_t*>(base + c.count);
+  int32_t* offset = reinterpret_cast<int32_t*>(base + c.offset);
+  int32_t* row_slot = reinterpret_cast<int32_t*>(base + c.row_slot);
+  int32_t* slot_row = reinterpret_cast<int32_t*>(base + c.slot_row);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + c.h);
+  float* y = reinterpret_cast<float*>(base + c.y);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
+  };
+
+  if (mark(0) != hipSuccess) return MOE_EHIP;
+  if (moe::launch_route(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
+                        idx, gate, nullptr, hs) != hipSuccess || mark(1) != hipSuccess)
+    return MOE_EHIP;
+  if (moe::launch_permute(s, idx, count, offset, row_slot, slot_row, hs) != hipSuccess ||
+      mark(2) != hipSuccess)
+    return MOE_EHIP;
+  st = run_ffn(s, x, count, offset, row_slot, w1, w3, w2, y, h, hs,
+               events ? MarkFn(mark) : MarkFn());
+  if (st != MOE_OK) return st;
+  if (moe::launch_combine(s, y, slot_row, gate, out, p->out_dtype == MOE_BF16, hs) != hipSuccess ||
+      mark(5) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

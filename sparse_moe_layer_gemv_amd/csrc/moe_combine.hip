@@ -1,0 +1,57 @@
+// Gate-weighted combine of the expert outputs.
+// "Mixtral of Experts", section 2.1, first display equation: the layer output
+// is the sum over experts of G(x)_i * E_i(x); with TopK gating only the K
+// chosen experts contribute.  out[t] = sum_k gate[t][k] * y_rows[slot_row[t*K+k]],
+// summed in slot order k = 0, 1, ... (a gather, no atomics, so it is
+// deterministic).  Bound by HBM: reads K fp32 rows and writes one row per token.
+#include "moe_device.hpp"
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kCombineThreads = 256;
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const float* __restrict__ y_rows, const int32_t* __restrict__ slot_row,
+    const float* __restrict__ gate, int D, int K, void* __restrict__ out) {
+  const int t = blockIdx.x;
+  for (int d = threadIdx.x * 4; d < D; d += kCombineThreads * 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+      const int r = slot_row[size_t(t) * K + k];
+      if (r < 0) continue;
+      const float g = gate[size_t(t) * K + k];
+      const f32x4 v = *reinterpret_cast<const f32x4*>(y_rows + size_t(r) * D + d);
+      acc[0] = fmaf(g, v[0], acc[0]);
+      acc[1] = fmaf(g, v[1], acc[1]);
+      acc[2] = fmaf(g, v[2], acc[2]);
+      acc[3] = fmaf(g, v[3], acc[3]);
+    }
+    if constexpr (OUT_BF16) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[0], acc[1]);
+      pk.y = pack_bf16x2(acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + size_t(t) * D + d) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + size_t(t) * D + d) = acc;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Shape& s, const float* y_rows, const int32_t* slot_row,
+                          const float* topk_gate, void* out, bool out_bf16, hipStream_t stream) {
+  if (s.T == 0) return hipSuccess;
+  if (out_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(s.T), dim3(kCombineThreads), 0, stream, y_rows,
+                       slot_row, topk_gate, s.D, s.K, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(s.T), dim3(kCombineThreads), 0, stream, y_rows,
+                       slot_row, topk_gate, s.D, s.K, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// Internal interface between the C ABI (moe_api.cpp) and the HIP kernels.
+// Nothing here is exported; every launcher enqueues on `stream` and returns
+// the launch status without synchronising.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Permuted-layout granule (rows per expert segment step); equals MOE_TILE_M.
+constexpr int kTileM = 256;
+// Largest T served by the weight-streaming (decode) expert path.
+constexpr int kDecodeMaxTokens = 32;
+// Token rows handled together by one decode pass (one 16x16 MFMA column block).
+constexpr int kDecodeRows = 16;
+
+struct Shape {
+  int T, D, H, n, K;
+  int64_t cap;  // rows of the permuted layout
+};
+
+hipError_t launch_route(const Shape& s, const uint16_t* x, const uint16_t* w_gate,
+                        int32_t* topk_idx, float* topk_gate, float* logits,
+                        hipStream_t stream);
+
+hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* expert_count,
+                          int32_t* expert_offset, int32_t* row_slot, int32_t* slot_row,
+                          hipStream_t stream);
+
+// Tiled matrix-core path: h = silu(x w1) * (x w3) per expert segment, then
+// y_rows = h w2.  h is bf16 [cap][H] in the workspace.
+hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_offset,
+                             const int32_t* row_slot, const uint16_t* w1, const uint16_t* w3,
+                             uint16_t* h, hipStream_t stream);
+hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, const uint16_t* h,
+                               const uint16_t* w2, float* y_rows, hipStream_t stream);
+
+// Weight-streaming path for small T (every touched expert's weights read once).
+hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
+                            const int32_t* expert_offset, const int32_t* row_slot,
+                            const uint16_t* w1, const uint16_t* w3, uint16_t* h,
+                            hipStream_t stream);
+hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
+                              const int32_t* expert_offset, const uint16_t* h,
+                              const uint16_t* w2, float* y_rows, hipStream_t stream);
+
+hipError_t launch_combine(const Shape& s, const float* y_rows, const int32_t* slot_row,
+                          const float* topk_gate, void* out, bool out_bf16, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,118 @@
+"""The libmoe C ABI on the CPU: the library loads, exports every function that
+include/libmoe.h declares, and rejects bad arguments before touching the GPU.
+No call here reaches a kernel launch (tokens == 0 returns before any HIP call,
+and every other call fails validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmoe.h")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    lib_path = os.path.join(ROOT, "sparse_moe_layer_gemv_amd", "libmoe.so")
+    if not os.path.exists(lib_path):
+        import runpy
+        runpy.run_path(os.path.join(ROOT, "sparse_moe_layer_gemv_amd", "_build.py"))["build"]()
+    import sparse_moe_layer_gemv_amd as m
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
+              "moe_workspace_bytes", "moe_capacity_rows", "moe_status_string",
+              "moe_decode_max_tokens"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(moe):
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(moe.lib, name)
+    assert set(moe.EXPORTED) == set(_declared_functions())
+
+
+def test_capacity_and_workspace(moe):
+    p = moe.problem(4096, 4096, 14336, 8, 2)
+    cap = moe.capacity_rows(p)
+    assert cap == ((8192 + 8 * 255 + 255) // 256) * 256
+    ws = moe.workspace_bytes(p)
+    # h (bf16) and y_rows (fp32) dominate
+    assert ws >= cap * (14336 * 2 + 4096 * 4)
+    assert ws < cap * (14336 * 2 + 4096 * 4) + 4 * 1024 * 1024
+    assert moe.capacity_rows(moe.problem(4096, 4096, 14336, 8, 9)) == -1   # K > n
+    assert moe.workspace_bytes(moe.problem(16, 4100, 14336, 8, 2)) == 0    # dim % 8
+    assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 65, 2)) == 0   # n > 64
+    assert moe.decode_max_tokens() >= 16
+
+
+def test_status_strings(moe):
+    for s in range(5):
+        assert moe.lib.moe_status_string(s)
+    assert moe.lib.moe_status_string(99) == b"unknown status"
+
+
+FAKE = 0x100000  # a 256-byte-aligned non-null address; validation never dereferences it
+
+
+def _fwd(moe, p, ptrs=None, ws=FAKE, ws_bytes=None):
+    ptrs = ptrs or {}
+    args = [ptrs.get(k, FAKE) for k in ("x", "wg", "w1", "w3", "w2", "out")]
+    if ws_bytes is None:
+        ws_bytes = moe.workspace_bytes(p)
+    return moe.lib.moe_forward(ctypes.byref(p), *args, None, None, ws, ws_bytes, None)
+
+
+def test_validation_errors(moe):
+    good = moe.problem(64, 128, 256, 8, 2)
+    assert _fwd(moe, moe.problem(0, 128, 256, 8, 2)) == moe.MOE_OK          # T = 0: no-op
+    assert _fwd(moe, moe.problem(-1, 128, 256, 8, 2)) == moe.MOE_EINVAL
+    assert _fwd(moe, moe.problem(64, 128, 256, 8, 0)) == moe.MOE_EINVAL     # K < 1
+    assert _fwd(moe, moe.problem(64, 128, 256, 8, 9)) == moe.MOE_EINVAL     # K > n
+    assert _fwd(moe, moe.problem(64, 130, 256, 8, 2)) == moe.MOE_EINVAL     # dim % 8
+    assert _fwd(moe, moe.problem(64, 128, 250, 8, 2)) == moe.MOE_EINVAL     # hidden % 8
+    assert _fwd(moe, moe.problem(64, 128, 256, 65, 2)) == moe.MOE_ENOTSUP   # n > 64
+    assert _fwd(moe, moe.problem(64, 128, 256, 8, 2, 7)) == moe.MOE_EINVAL  # out dtype
+    assert _fwd(moe, good, {"x": 0}) == moe.MOE_EINVAL                      # null
+    assert _fwd(moe, good, {"w1": FAKE + 8}) == moe.MOE_EINVAL              # misaligned
+    assert _fwd(moe, good, ws=0) == moe.MOE_EWORKSPACE
+    assert _fwd(moe, good, ws_bytes=moe.workspace_bytes(good) - 1) == moe.MOE_EWORKSPACE
+    assert _fwd(moe, good, ws=FAKE + 16) == moe.MOE_EINVAL                  # ws not 256-aligned
+    assert moe.lib.moe_forward(None, *([FAKE] * 6), None, None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
+
+
+def test_stage_validation_errors(moe):
+    p = moe.problem(64, 128, 256, 8, 2)
+    L = moe.lib
+    assert L.moe_route(ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, None) == moe.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE + 4, None) == moe.MOE_EINVAL
+    assert L.moe_permute(ctypes.byref(p), FAKE, FAKE, FAKE, 0, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_grouped_ffn(ctypes.byref(p), *([FAKE] * 8), FAKE, 16, None) == moe.MOE_EWORKSPACE
+    assert L.moe_combine(ctypes.byref(p), FAKE, FAKE, FAKE, 0, None) == moe.MOE_EINVAL
+    z = moe.problem(0, 128, 256, 8, 2)
+    assert L.moe_route(ctypes.byref(z), 0, 0, 0, 0, None, None) == moe.MOE_OK
+    assert L.moe_combine(ctypes.byref(z), 0, 0, 0, 0, None) == moe.MOE_OK
+
+
+def test_binding_rejects_cpu_tensors(moe):
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.route(x, torch.zeros((128, 8), dtype=torch.bfloat16), 2,
+                  topk_idx=torch.zeros((4, 2), dtype=torch.int32),
+                  topk_gate=torch.zeros((4, 2)))

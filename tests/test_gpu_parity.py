@@ -1,0 +1,183 @@
+"""GPU parity of every libmoe entry point against the fp64 oracle, at sizes the
+oracle finishes in seconds: several row/column/contraction tiles, ragged
+tails, both expert paths (weight streaming for T <= 32, matrix-core tiles
+above), forced skewed and empty-expert routings, K and n variants."""
+import numpy as np
+import pytest
+
+import moe_synth
+from oracle import moe_ref, parity
+from tests.gpu_helpers import dev_bf16, dev_i32, expected_permutation, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_moe_layer_gemv_amd as m
+    return m
+
+
+def _upload(L):
+    return dict(x=dev_bf16(L.x), wg=dev_bf16(L.w_gate), w1=dev_bf16(L.w1), w3=dev_bf16(L.w3),
+                w2=dev_bf16(L.w2))
+
+
+def _check_forward(moe, L, label):
+    import torch
+    d = _upload(L)
+    T, D, H, n, K = L.shape
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda:0")
+    out = moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], K, topk_idx=idx, topk_gate=gate)
+    out_h, idx_h, gate_h = host(out), host(idx), host(gate)
+    logits = moe_ref.router_logits(L.x, L.w_gate)
+    rr = parity.check_routing(logits, K, idx_h, gate_h)
+    print(f"[{label}] T={T} D={D} H={H} n={n} K={K} routing: {rr}")
+    assert rr.ok, rr
+    ref = moe_ref.moe_layer(L.x, L.w_gate, L.w1, L.w3, L.w2, K, forced_idx=rr.forced_idx)
+    orep = parity.check_output(ref["y"], out_h)
+    print(f"[{label}] output: max/RMS={orep.max_rel:.3e} mean/RMS={orep.mean_rel:.3e}")
+    assert orep.ok, orep
+    return d, out
+
+
+SHAPES = [
+    # label, T, D, H, n, K, seed
+    ("tiny", 64, 128, 256, 8, 2, None),
+    ("ragged_dims", 300, 200, 328, 8, 2, 11),
+    ("multi_tile", 1500, 512, 768, 8, 2, 12),
+    ("decode_t1", 1, 512, 1024, 8, 2, 13),
+    ("decode_t2", 2, 256, 384, 8, 2, 14),
+    ("decode_t16", 16, 512, 1024, 8, 2, 15),
+    ("decode_t17", 17, 512, 1024, 8, 2, 16),
+    ("decode_t32", 32, 384, 640, 8, 2, 17),
+    ("mfma_t33", 33, 512, 1024, 8, 2, 18),
+    ("k1_switch", 200, 256, 512, 8, 1, 19),
+    ("n16_k4", 130, 256, 384, 16, 4, 20),
+    ("n6_k3", 90, 136, 200, 6, 3, 21),
+    ("n64_k2", 400, 128, 256, 64, 2, 22),
+]
+
+
+@pytest.mark.parametrize("label,T,D,H,n,K,seed", SHAPES, ids=[s[0] for s in SHAPES])
+def test_forward_parity(moe, label, T, D, H, n, K, seed):
+    if seed is None:
+        L = moe_synth.make_workload("tiny")
+    else:
+        L = moe_synth.make_layer(T, D, H, n, K, seed=seed)
+    _check_forward(moe, L, label)
+
+
+def test_route_stage_and_logits(moe):
+    import torch
+    L = moe_synth.make_layer(777, 4096, 64, 8, 2, seed=31)
+    d = _upload(L)
+    T = 777
+    logits = torch.empty((T, 8), dtype=torch.float32, device="cuda:0")
+    idx, gate = moe.route(d["x"], d["wg"], 2, logits=logits)
+    ref = moe_ref.router_logits(L.x, L.w_gate)
+    lg = host(logits)
+    # fp32 accumulation of 4096 products of magnitude ~1/64
+    assert np.abs(lg - ref).max() < 2e-5
+    rr = parity.check_routing(ref, 2, host(idx), host(gate))
+    assert rr.ok, rr
+
+
+def test_permute_stage_is_exact(moe):
+    rng = np.random.default_rng(5)
+    n, K = 8, 2
+    for T in (1, 63, 64, 65, 128, 1000, 5000, 9000):
+        idx = np.stack([rng.choice(n, size=K, replace=False) for _ in range(T)]).astype(np.int32)
+        p = moe.problem(T, 8, 8, n, K)
+        cap = moe.capacity_rows(p)
+        r = moe.permute(dev_i32(idx), n)
+        cnt, off, rs, sr = expected_permutation(idx, n, moe.TILE_M, cap)
+        assert np.array_equal(host(r["expert_count"]), cnt)
+        assert np.array_equal(host(r["expert_offset"]), off)
+        assert np.array_equal(host(r["row_slot"]), rs)
+        assert np.array_equal(host(r["slot_row"]), sr)
+
+
+def test_permute_drops_out_of_range_experts(moe):
+    idx = np.array([[0, 9], [-1, 3], [3, 0]], np.int32)
+    r = moe.permute(dev_i32(idx), 8)
+    sr = host(r["slot_row"])
+    assert sr[1] == -1 and sr[2] == -1
+    assert host(r["expert_count"]).tolist() == [2, 0, 0, 2, 0, 0, 0, 0]
+
+
+FORCED = [
+    # label, forced expert choice per token (K=2), T
+    ("all_on_expert3", lambda T: np.tile([[3, 5]], (T, 1)), 700),
+    ("counts_255_256_257", None, 0),
+    ("one_expert_k1", lambda T: np.full((T, 1), 6), 600),
+]
+
+
+def _forced_counts_case():
+    # expert 0: 255 slots, expert 1: 256, expert 2: 257, others empty (K=1)
+    return np.concatenate([np.zeros(255), np.ones(256), np.full(257, 2)]).astype(np.int32)[:, None]
+
+
+@pytest.mark.parametrize("label,make,T", FORCED, ids=[f[0] for f in FORCED])
+def test_grouped_ffn_forced_routing(moe, label, make, T):
+    import torch
+    idx = _forced_counts_case() if make is None else np.asarray(make(T), np.int32)
+    T, K = idx.shape
+    D, H, n = 256, 384, 8
+    L = moe_synth.make_layer(T, D, H, n, K, seed=41)
+    d = _upload(L)
+    perm = moe.permute(dev_i32(idx), n)
+    y_rows = moe.grouped_ffn(d["x"], perm["expert_count"], perm["expert_offset"], perm["row_slot"],
+                             d["w1"], d["w3"], d["w2"], K)
+    ref = moe_ref.moe_layer(L.x, L.w_gate, L.w1, L.w3, L.w2, K, forced_idx=idx, return_slots=True)
+    sr = host(perm["slot_row"])
+    got = host(y_rows)[sr].reshape(T, K, D)
+    orep = parity.check_output(ref["E"], got)
+    print(f"[{label}] slots max/RMS={orep.max_rel:.3e} mean/RMS={orep.mean_rel:.3e}")
+    assert orep.ok, orep
+    # combine of the GPU's expert rows with the oracle's gates, against fp64
+    gate = torch.from_numpy(ref["gate"].astype(np.float32)).to("cuda:0")
+    out = moe.combine(y_rows, perm["slot_row"], gate)
+    want = (ref["gate"].astype(np.float32).astype(np.float64)[:, :, None] * got).sum(axis=1)
+    assert np.abs(host(out) - want).max() <= 1e-6 * np.abs(want).max()
+
+
+def test_forward_is_deterministic_and_bf16_output_is_rne_of_fp32(moe):
+    import torch
+    L = moe_synth.make_layer(1000, 512, 768, 8, 2, seed=51)
+    d = _upload(L)
+    a = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2))
+    b = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, out_dtype=moe.MOE_BF16))
+    assert np.array_equal(c, moe_synth.bf16_bits(a))
+
+
+def test_outputs_do_not_write_past_their_end(moe):
+    import torch
+    L = moe_synth.make_layer(100, 256, 384, 8, 2, seed=61)
+    d = _upload(L)
+    guard = 64
+    out_buf = torch.full((100 * 256 + guard,), 12345.0, dtype=torch.float32, device="cuda:0")
+    idx_buf = torch.full((200 + guard,), -777, dtype=torch.int32, device="cuda:0")
+    gate_buf = torch.full((200 + guard,), 7.0, dtype=torch.float32, device="cuda:0")
+    moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, out=out_buf[:25600].view(100, 256),
+                topk_idx=idx_buf[:200].view(100, 2), topk_gate=gate_buf[:200].view(100, 2))
+    assert np.all(host(out_buf)[25600:] == 12345.0)
+    assert np.all(host(idx_buf)[200:] == -777)
+    assert np.all(host(gate_buf)[200:] == 7.0)
+
+
+def test_zero_tokens_is_a_noop(moe):
+    import torch
+    L = moe_synth.make_layer(4, 128, 256, 8, 2, seed=71)
+    d = _upload(L)
+    out = torch.empty((0, 128), dtype=torch.float32, device="cuda:0")
+    moe.forward(d["x"][:0], d["wg"], d["w1"], d["w3"], d["w2"], 2, out=out,
+                workspace=torch.empty(256, dtype=torch.uint8, device="cuda:0"))
+    torch.cuda.synchronize()
