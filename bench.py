@@ -1,0 +1,270 @@
+"""Benchmark of the Mixtral sparse MoE layer (libmoe) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole layer (router, permute, both expert products,
+combine) over one batch of synthetic Mixtral-shape input already resident in
+HBM.  Workloads (seeded, see moe_synth): prefill (T=4096, the default), decode
+(T=16), skewed (T=4096, ~60% of token-slots on two experts), large (T=32768
+fed as 4 chunks of 8192 through one workspace), tiny.
+
+Prints one JSON line.  Per-stage times come from HIP events recorded on the
+layer's stream between the stages inside the timed steps; the roofline object
+is for the dominant kernel (the first expert product: x.w1, x.w3 + silu).
+The cpu_baseline object times the fp64 oracle on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_synth  # noqa: E402
+
+METRIC = "MoE-layer tokens/sec + TFLOP/s (% MFMA peak), Mixtral shape, top-2 of 8, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must do; padding and skipped experts excluded)
+# ---------------------------------------------------------------------------
+def layer_flops(T, D, H, n, K):
+    """2*T*K*3*D*H expert multiply-adds x2 plus the router's 2*T*D*n."""
+    return 2 * T * K * 3 * D * H + 2 * T * D * n
+
+
+def up_flops(T, D, H, K):
+    return 2 * 2 * T * K * D * H
+
+
+def up_weight_bytes(touched, D, H):
+    return touched * 2 * D * H * 2
+
+
+def mixtral_params(dim=4096, n_layers=32, head_dim=128, hidden=14336, n_heads=32,
+                   n_kv_heads=8, vocab=32000, n_experts=8, top_k=2):
+    """(total, active) parameters of the whole model from Table 1 shapes; used to
+    check the FLOP/byte accounting against the pages' 46.7B / 13B."""
+    attn = dim * n_heads * head_dim * 2 + dim * n_kv_heads * head_dim * 2
+    expert = 3 * dim * hidden
+    router = dim * n_experts
+    norms = 2 * dim
+    per_layer_total = attn + n_experts * expert + router + norms
+    per_layer_active = attn + top_k * expert + router + norms
+    emb = 2 * vocab * dim + dim
+    return n_layers * per_layer_total + emb, n_layers * per_layer_active + emb
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime's C API (timing on the layer's own stream)
+# ---------------------------------------------------------------------------
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self, count):
+        out = []
+        for _ in range(count):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(ev.value)
+        self.made += out
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+        self.made = []
+
+
+STAGES = ("route", "permute", "up", "down", "combine")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+
+def cpu_baseline(name, inputs, sample_tokens, min_seconds=10.0):
+    """Time the fp64 oracle (as it stands) on the first `sample_tokens` tokens,
+    repeated until at least `min_seconds` of wall time have passed."""
+    from threadpoolctl import threadpool_info
+    from oracle import moe_ref
+    L = inputs
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        moe_ref.moe_layer(L.x[:sample_tokens], L.w_gate, L.w1, L.w3, L.w2, L.K)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = max(threads) if threads else 1
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": reps * sample_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of the {name} workload with its full weights, "
+                      f"fp64 numpy oracle run {reps}x, {dt:.1f} s wall", "cpu": cpu}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill", choices=sorted(moe_synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens for the oracle timing (default: a bounded sample per workload)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "libmoe is a single-GPU build: each GPU runs the whole layer "
+                                   "on its own share of tokens and there is no cross-GPU step; "
+                                   "run with --gpus 1"}))
+        return 2
+
+    import torch
+    import sparse_moe_layer_gemv_amd as moe
+
+    w = moe_synth.WORKLOADS[args.workload]
+    T, D, H, n, K = w.T, w.D, w.H, w.n, w.K
+    chunk = w.chunk or T
+    log(f"[bench] generating {args.workload} inputs T={T} D={D} H={H} n={n} K={K}")
+    t0 = time.perf_counter()
+    L = moe_synth.make_workload(args.workload)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    x, wg, w1, w3, w2 = (to_dev(a) for a in (L.x, L.w_gate, L.w1, L.w3, L.w2))
+    out = torch.empty((T, D), dtype=torch.float32, device="cuda:0")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(moe.workspace_bytes(moe.problem(chunk, D, H, n, K)), dtype=torch.uint8,
+                     device="cuda:0")
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+    n_chunks = (T + chunk - 1) // chunk
+
+    def step(events_for_step=None):
+        for c in range(n_chunks):
+            c0, c1 = c * chunk, min(T, (c + 1) * chunk)
+            e6 = None if events_for_step is None else events_for_step[c]
+            moe.forward(x[c0:c1], wg, w1, w3, w2, K, out=out[c0:c1], topk_idx=idx[c0:c1],
+                        topk_gate=gate[c0:c1], workspace=ws, stream=stream, events=e6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    evs = [[ev.create(6) for _ in range(n_chunks)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"[bench] timed region done: {wall * 1e3:.2f} ms")
+
+    stage_ms = {k: [] for k in STAGES}
+    for s in range(args.steps):
+        for c in range(n_chunks):
+            e6 = evs[s][c]
+            for i, k in enumerate(STAGES):
+                stage_ms[k].append(ev.elapsed_ms(e6[i], e6[i + 1]))
+    ev.close()
+    # per-launch averages (one launch of each stage per chunk)
+    stage_avg = {k: float(np.mean(v)) for k, v in stage_ms.items()}
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = T / (ms_per_step / 1e3)
+    flops = layer_flops(T, D, H, n, K)
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=n)
+    touched = int((counts > 0).sum())
+    decode = T <= moe.decode_max_tokens()
+    if decode:
+        # the weight-streaming kernel reads w1 and w3 of every touched expert once
+        per_launch = up_weight_bytes(touched, D, H)
+        achieved = per_launch / (stage_avg["up"] / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "decode_up",
+                "algorithmic_per_launch": per_launch}
+    else:
+        per_launch = up_flops(chunk, D, H, K)
+        achieved = per_launch / (stage_avg["up"] / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "grouped_up",
+                "algorithmic_per_launch": per_launch}
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "dim": D, "hidden": H,
+                   "n_experts": n, "top_k": K, "chunk": chunk, "parallelism": "none"},
+        "tflops": tflops,
+        "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
+        "stage_ms": stage_avg,
+        "expert_counts": counts.tolist(),
+        "roofline": roof,
+    }
+    if decode:
+        total_bytes = touched * 3 * D * H * 2 + T * D * 2 + D * n * 2 + T * D * 4 + T * K * 8
+        rec["hbm_gbs_layer"] = total_bytes / (ms_per_step / 1e3) / 1e9
+        rec["hbm_peak_frac_layer"] = rec["hbm_gbs_layer"] / PEAK_HBM_GBS
+
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or min(T, 4096)
+        log(f"[bench] timing the fp64 oracle on {sample} tokens")
+        rec["cpu_baseline"] = cpu_baseline(args.workload, L, sample)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
