@@ -33,7 +33,10 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
       (P + int64_t(p->n_experts) * (MOE_TILE_M - 1) + MOE_TILE_M - 1) / MOE_TILE_M * MOE_TILE_M;
   // row indices and element offsets inside one expert are int32 on the device
   if (cap >= (int64_t(1) << 31)) return MOE_ENOTSUP;
-  if (int64_t(p->dim) * p->hidden >= (int64_t(1) << 31)) return MOE_ENOTSUP;
+  // buffer resources address x, one expert's weight matrix and one row tile
+  // of h with 32-bit byte offsets
+  if (int64_t(p->dim) * p->hidden * 2 >= (int64_t(1) << 31)) return MOE_ENOTSUP;
+  if (int64_t(p->tokens) * p->dim * 2 >= (int64_t(1) << 31)) return MOE_ENOTSUP;
   s->T = p->tokens;
   s->D = p->dim;
   s->H = p->hidden;

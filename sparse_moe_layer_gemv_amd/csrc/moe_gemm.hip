@@ -11,25 +11,32 @@
 //
 // Tiling (both kernels): a 256-thread workgroup (4 wavefronts, one per SIMD)
 // owns a 256-row x 256-column output tile and walks the contraction axis in
-// 64-wide steps through a double-buffered LDS stage (2 x 64 KiB).  Each wave
-// owns a 128 x 128 sub-tile held as 4 x 4 accumulators of
-// v_mfma_f32_32x32x16_bf16 (256 fp32 per lane).  In the up kernel the 256
-// columns are 128 columns of w1 and the same 128 columns of w3, so each wave
-// holds a and b for identical (row, column) pairs and applies silu(a)*b in
-// registers before a single bf16 rounding.
+// 64-wide steps through two LDS stages of 64 KiB.  Each wave owns a 128 x 128
+// sub-tile held as 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (256 fp32
+// per lane, in the accumulation registers).  In the up kernel the 256 columns
+// are 128 columns of w1 and the same 128 columns of w3, so each wave holds a
+// and b for identical (row, column) pairs and applies silu(a)*b in registers
+// before a single bf16 rounding.
 //
-// Layouts: weights are row-major with the output axis contiguous ([D][H],
-// [H][D]), but the matrix-core operand wants 8 consecutive contraction
-// elements per lane.  Each thread therefore loads an 8 x 8 block (8 rows of
-// 16 bytes, coalesced along the output axis), transposes it in registers with
-// byte permutes, and stores 8 contraction-contiguous 16-byte chunks into LDS.
-// LDS rows are 128 bytes (64 bf16 of the contraction axis) with the 16-byte
-// chunk index XOR-swizzled so both the transposed stores and the operand
-// reads spread over all banks.
-//
-// The weight operand is fed to the matrix core as the "A" (row) side and the
-// activations as "B", so each lane's accumulator holds 4 consecutive output
-// columns of one token row: h is stored as 8-byte and y as 16-byte vectors.
+// Data path: both operands go from HBM straight into LDS with buffer loads in
+// LDS-DMA mode (no staging registers, no LDS store instructions).  A DMA
+// instruction writes 64 lanes x 16 bytes contiguously, so the LDS layout is
+// chosen through the global address each lane fetches:
+//  - activations (contraction-contiguous rows) land as 128-byte rows with the
+//    16-byte chunk index XOR-swizzled by the row, and are read back as
+//    128-bit fragments;
+//  - weights are row-major with the OUTPUT axis contiguous ([D][H], [H][D]);
+//    they land untransposed as 256-byte rows (64 contraction rows x 128
+//    columns per sub-tile, chunks swizzled by the row), and the matrix-core
+//    operand (8 consecutive contraction elements per lane) is formed by the
+//    gfx950 transposing LDS read ds_read_b64_tr_b16: each 16-lane group reads
+//    a 4 x 16 block and every lane receives 4 contraction elements of one
+//    column.
+// Rows of padding get an out-of-range buffer offset, which the hardware
+// returns as zeros.  The weight fragments are the matrix core's "A" (row)
+// side and the activations "B", so each lane's accumulator holds 4
+// consecutive output columns of one token row: h is stored as 8-byte and y as
+// 16-byte vectors.
 //
 // Workgroup order: the hardware hands workgroup ids to the 8 XCDs round-robin,
 // and each XCD has its own L2.  The block id is remapped so every XCD works on
@@ -42,52 +49,53 @@
 namespace moe {
 namespace {
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
 constexpr int BM = 256;          // rows (token-slots) per tile
 constexpr int BK = 64;           // contraction step
-constexpr int BNC = 256;         // output columns per tile held in LDS
+constexpr int SUBN = 128;        // columns per weight sub-tile
 constexpr int NTHR = 256;
-constexpr int A_BYTES = BM * BK * 2;    // 32 KiB
-constexpr int B_BYTES = BNC * BK * 2;   // 32 KiB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int A_BYTES = BM * BK * 2;        // 32 KiB
+constexpr int B_SUB_BYTES = BK * SUBN * 2;  // 16 KiB
 constexpr int GROUP_M = 4;
+constexpr uint32_t kOOB = 0x80000000u;      // buffer offset beyond any resource (< 2^31 bytes): reads as 0
+constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data (gfx9 family)
 
 static_assert(BM == kTileM, "segment granule must equal the row tile");
 
-// LDS byte offset of 16-byte chunk c (0..7) of activation row m.
-__device__ __forceinline__ uint32_t a_off(int m, int c) {
-  return uint32_t(m) * 128u + (uint32_t((c ^ (m & 7))) << 4);
-}
-// LDS byte offset of 16-byte chunk c of weight column n (contraction-contiguous).
-__device__ __forceinline__ uint32_t b_off(int n, int c) {
-  return uint32_t(n) * 128u + (uint32_t(c ^ (n & 7) ^ ((n >> 3) & 7)) << 4);
+// Two LDS stages as distinct objects, so the compiler can tell the DMA into
+// one stage from the reads of the other.
+__shared__ __attribute__((aligned(1024))) uint8_t g_a0[A_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t g_a1[A_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t g_b0[2 * B_SUB_BYTES];
+__shared__ __attribute__((aligned(1024))) uint8_t g_b1[2 * B_SUB_BYTES];
+
+__device__ __forceinline__ lds_u8* lds(uint8_t* p) { return (lds_u8*)(p); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
 }
 
-__device__ __forceinline__ void lds_store16(uint8_t* smem, uint32_t off, uint4 v) {
-  *reinterpret_cast<uint4*>(smem + off) = v;
-}
-__device__ __forceinline__ bf16x8 lds_load16(const uint8_t* smem, uint32_t off) {
-  return as_bf16x8(*reinterpret_cast<const uint4*>(smem + off));
+// 16 bytes per lane from buffer offset voff + soff into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, soff, 0, 0);
 }
 
-// Transpose an 8x8 block of bf16: in[j] holds row j (8 columns), out[c] gets
-// column c (8 rows).  One byte-permute per output word.
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-  uint32_t w[8][4];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    w[j][0] = in[j].x; w[j][1] = in[j].y; w[j][2] = in[j].z; w[j][3] = in[j].w;
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = w[2 * p][c >> 1];
-      const uint32_t hi = w[2 * p + 1][c >> 1];
-      o[p] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    out[c] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+__device__ __forceinline__ bf16x8 lds_read128(const uint8_t* base, uint32_t off) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(base + off));
+}
+
+// Weight fragment: two transposing 64-bit reads, 4 contraction rows apart.
+__device__ __forceinline__ bf16x8 lds_read_wfrag(uint8_t* base, uint32_t off) {
+  v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(lds(base) + off));
+  v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(lds(base) + off + 4 * SUBN * 2));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // XCD-aware tile mapping.  Workgroup L runs on XCD L % 8.  Valid workgroups
@@ -116,27 +124,122 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offset,
   return e;
 }
 
-// One 64-wide contraction step of the wave's 128x128 sub-tile.
-//   smem_a: activation stage, smem_b: weight stage
-//   a_row0: first activation row of this wave, b_col0[j]: first weight column of fragment j
-__device__ __forceinline__ void mma_stage(const uint8_t* smem_a, const uint8_t* smem_b, int lane,
-                                          int a_row0, const int (&b_col)[4], f32x16 (&acc)[4][4]) {
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+// Per-lane state of one tile: DMA offsets and LDS read offsets.
+struct TileCtx {
+  __amdgpu_buffer_rsrc_t ra;      // activation rows
+  __amdgpu_buffer_rsrc_t rb;      // this wave's weight sub-tile
+  uint32_t a_voff[8];             // per DMA instruction (row), lane part
+  uint32_t b_voff;                // lane part of the weight DMA offset
+  uint32_t b_row_bytes;           // bytes per weight row (N * 2)
+  int a_dst, b_dst;               // wave's LDS destination offsets within a stage
+  uint32_t x_rd[4];               // activation fragment read offsets, per kk
+  uint32_t w_rd[4];               // weight fragment read offsets, per fragment j
+};
+
+template <bool EVEN>
+__device__ __forceinline__ void issue_stage(const TileCtx& c, uint8_t* sa, uint8_t* sb, int k0) {
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    const int c = kk * 2 + hi;
-    bf16x8 xf[4], wf[4];
+  for (int i = 0; i < 8; ++i) dma16(c.ra, lds(sa) + c.a_dst + i * 8 * 128, c.a_voff[i], k0 * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xf[i] = lds_load16(smem_a, a_off(a_row0 + i * 32 + l32, c));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wf[j] = lds_load16(smem_b, b_off(b_col[j] + l32, c));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t rows = uint32_t(k0 + i * 4) * c.b_row_bytes;
+    if (EVEN)
+      dma16(c.rb, lds(sb) + c.b_dst + i * 4 * SUBN * 2, c.b_voff, rows);
+    else
+      dma16(c.rb, lds(sb) + c.b_dst + i * 4 * SUBN * 2, c.b_voff + rows, 0);
   }
+}
+
+__device__ __forceinline__ void read_frags(const TileCtx& c, uint8_t* sa, uint8_t* sb, int kk,
+                                           bf16x8 (&xf)[4], bf16x8 (&wf)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wf[j] = lds_read_wfrag(sb, c.w_rd[j] + kk * 16 * SUBN * 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xf[i] = lds_read128(sa, c.x_rd[kk] + i * 32 * 128);
+}
+
+__device__ __forceinline__ void mma16(const bf16x8 (&xf)[4], const bf16x8 (&wf)[4],
+                                      f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+}
+
+// One 64-deep stage: fragments of step kk+1 are read while the 16 products of
+// step kk run; scheduling barriers keep the two register sets from merging.
+__device__ __forceinline__ void compute_stage(const TileCtx& c, uint8_t* sa, uint8_t* sb,
+                                              f32x16 (&acc)[4][4]) {
+  bf16x8 x0[4], w0[4], x1[4], w1[4];
+  read_frags(c, sa, sb, 0, x0, w0);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(c, sa, sb, 1, x1, w1);
+  mma16(x0, w0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(c, sa, sb, 2, x0, w0);
+  mma16(x1, w1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(c, sa, sb, 3, x1, w1);
+  mma16(x0, w0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  mma16(x1, w1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Main loop over the contraction axis with two static LDS stages: the DMA of
+// step k+1 runs while step k is multiplied out of the other stage.
+template <bool EVEN>
+__device__ __forceinline__ void run_tile(const TileCtx& c, int ksteps, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  issue_stage<EVEN>(c, g_a0, g_b0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int ks = 0;
+  for (; ks + 2 <= ksteps; ks += 2) {
+    issue_stage<EVEN>(c, g_a1, g_b1, (ks + 1) * BK);
+    compute_stage(c, g_a0, g_b0, acc);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (ks + 2 < ksteps) issue_stage<EVEN>(c, g_a0, g_b0, (ks + 2) * BK);
+    compute_stage(c, g_a1, g_b1, acc);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (ks < ksteps) compute_stage(c, g_a0, g_b0, acc);  // odd number of steps
+}
+
+// Lane-dependent LDS offsets shared by both kernels.
+//   sub[j], cb[j]: weight sub-tile and first column (within it) of fragment j
+__device__ __forceinline__ void setup_reads(TileCtx& c, int lane, int wm, const int (&sub)[4],
+                                            const int (&cb)[4]) {
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int m = wm * 128 + l32;
+    c.x_rd[kk] = uint32_t(m * 128 + (((2 * kk + hi) ^ (m & 7)) << 4));
+  }
+  const int g = lane >> 4, j16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kr = 8 * (g >> 1) + (j16 >> 2);                    // contraction row in the step
+    const int chunk = ((cb[j] >> 3) ^ ((j16 >> 2) << 2)) + 2 * (g & 1) + ((j16 & 3) >> 1);
+    c.w_rd[j] = uint32_t(sub[j] * B_SUB_BYTES + kr * SUBN * 2 + chunk * 16 + (j16 & 1) * 8);
+  }
+}
+
+// Lane part of the weight DMA: wave `wave` fills rows (wave&1)*32 .. +32 of
+// sub-tile wave>>1; lane l covers row +l/16, physical chunk l%16.
+__device__ __forceinline__ void setup_b_dma(TileCtx& c, int lane, int wave, int col0, int n_cols) {
+  const int kr = (wave & 1) * 32 + (lane >> 4);
+  const int lc = (lane & 15) ^ ((lane >> 4) << 2);
+  c.b_row_bytes = uint32_t(n_cols) * 2;
+  c.b_voff = uint32_t(kr) * c.b_row_bytes + uint32_t(col0 + lc * 8) * 2;
+  c.b_dst = (wave >> 1) * B_SUB_BYTES + (wave & 1) * 32 * SUBN * 2;
 }
 
 // ---------------------------------------------------------------------------
@@ -146,95 +249,47 @@ template <bool EVEN>
 __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ expert_offset,
     const int32_t* __restrict__ row_slot, const uint16_t* __restrict__ w1,
-    const uint16_t* __restrict__ w3, uint16_t* __restrict__ h, int D, int H, int n, int K) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
-
+    const uint16_t* __restrict__ w3, uint16_t* __restrict__ h, int T, int D, int H, int n, int K) {
   const int mt_count = expert_offset[n] / BM;
-  const int nt_count = (H + 127) / 128;
+  const int nt_count = (H + SUBN - 1) / SUBN;
   int mt, nt;
   if (!map_tile(blockIdx.x, mt_count, nt_count, mt, nt)) return;
   const int row0 = mt * BM;
   const int e = expert_of_row(expert_offset, n, row0);
-  const int n0 = nt * 128;
+  const int n0 = nt * SUBN;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // activation loads: chunk ac of rows ar + 32 i
-  const int ac = tid & 7;
-  const int ar = tid >> 3;
-  const uint16_t* xrow[8];
-  bool xvalid[8];
+  TileCtx c;
+  c.ra = make_rsrc(x, uint32_t(T) * D * 2);
+  const size_t wsz = size_t(D) * H;
+  c.rb = make_rsrc(((wave >> 1) ? w3 : w1) + size_t(e) * wsz, uint32_t(wsz * 2));
+  // activation DMA: instruction i covers rows wave*64 + i*8 .. +8; lane l
+  // fetches row +l/8, logical chunk (l%8) ^ (row%8)
+  const int lc = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int slot = row_slot[row0 + ar + 32 * i];
-    xvalid[i] = slot >= 0;
-    const int tok = xvalid[i] ? slot / K : 0;
-    xrow[i] = x + size_t(tok) * D + ac * 8;
+    const int slot = row_slot[row0 + wave * 64 + i * 8 + (lane >> 3)];
+    const uint32_t tok = uint32_t(max(slot, 0)) / uint32_t(K);
+    c.a_voff[i] = slot >= 0 ? tok * uint32_t(D) * 2 + lc * 16 : kOOB;
   }
-  // weight loads: matrix wmat, chunk row-block kc (8 rows), column block nb (8 cols)
-  const int wmat = wave >> 1;
-  const int kc = ((wave & 1) << 2) | (lane >> 4);
-  const int nb = lane & 15;
-  const uint16_t* wbase = (wmat ? w3 : w1) + size_t(e) * D * H + size_t(kc * 8) * H + n0 + nb * 8;
-  const bool wcol_ok = EVEN || (n0 + nb * 8 < H);
-
-  uint4 ra[8], rb[8];
-  auto load_stage = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = xvalid[i] && (EVEN || k0 + ac * 8 < D);
-      ra[i] = ok ? *reinterpret_cast<const uint4*>(xrow[i] + k0) : make_uint4(0, 0, 0, 0);
-    }
-    const bool kok = EVEN || (k0 + kc * 8 < D);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      rb[j] = (wcol_ok && kok) ? *reinterpret_cast<const uint4*>(wbase + size_t(k0 + j) * H)
-                               : make_uint4(0, 0, 0, 0);
-  };
-  auto store_stage = [&](uint8_t* st) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lds_store16(st, a_off(ar + 32 * i, ac), ra[i]);
-    uint4 tb[8];
-    transpose8x8(rb, tb);
-    uint8_t* sb = st + A_BYTES;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) lds_store16(sb, b_off(wmat * 128 + nb * 8 + c, kc), tb[c]);
-  };
+  c.a_dst = wave * 64 * 128;
+  setup_b_dma(c, lane, wave, n0, H);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int sub[4] = {0, 0, 1, 1};
+  const int cb[4] = {wn * 64, wn * 64 + 32, wn * 64, wn * 64 + 32};
+  setup_reads(c, lane, wm, sub, cb);
 
   f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  run_tile<EVEN>(c, (D + BK - 1) / BK, acc);
 
-  const int wm = wave >> 1, wn = wave & 1;
-  const int a_row0 = wm * 128;
-  const int b_col[4] = {wn * 64, wn * 64 + 32, 128 + wn * 64, 128 + wn * 64 + 32};
-
-  const int ksteps = (D + BK - 1) / BK;
-  load_stage(0);
-  store_stage(smem);
-  __syncthreads();
-  for (int ks = 0; ks < ksteps; ++ks) {
-    uint8_t* cur = smem + (ks & 1) * STAGE_BYTES;
-    uint8_t* nxt = smem + ((ks + 1) & 1) * STAGE_BYTES;
-    const bool more = ks + 1 < ksteps;
-    if (more) load_stage((ks + 1) * BK);
-    mma_stage(cur, cur + A_BYTES, lane, a_row0, b_col, acc);
-    if (more) store_stage(nxt);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds token row (a_row0 + 32 i + lane%32) and, per
-  // register quad q, 4 consecutive columns starting at 8 q + 4 (lane/32)
+  // lane holds token row (wm*128 + 32 i + lane%32) and, per register quad q,
+  // 4 consecutive columns starting at 8 q + 4 (lane/32)
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = row0 + a_row0 + i * 32 + l32;
+    const int m = row0 + wm * 128 + i * 32 + l32;
     uint16_t* hrow = h + size_t(m) * H;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -244,11 +299,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
         if (!EVEN && col >= H) continue;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = acc[i][jj][q * 4 + r];
-          const float b = acc[i][jj + 2][q * 4 + r];
-          v[r] = silu(a) * b;
-        }
+        for (int r = 0; r < 4; ++r) v[r] = silu(acc[i][jj][q * 4 + r]) * acc[i][jj + 2][q * 4 + r];
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
@@ -265,88 +316,47 @@ template <bool EVEN>
 __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
     const int32_t* __restrict__ expert_offset, const uint16_t* __restrict__ h,
     const uint16_t* __restrict__ w2, float* __restrict__ y, int D, int H, int n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
-
   const int mt_count = expert_offset[n] / BM;
-  const int nt_count = (D + BNC - 1) / BNC;
+  const int nt_count = (D + 2 * SUBN - 1) / (2 * SUBN);
   int mt, nt;
   if (!map_tile(blockIdx.x, mt_count, nt_count, mt, nt)) return;
   const int row0 = mt * BM;
   const int e = expert_of_row(expert_offset, n, row0);
-  const int n0 = nt * BNC;
+  const int n0 = nt * 2 * SUBN;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int ac = tid & 7;
-  const int ar = tid >> 3;
-  const uint16_t* hrow = h + size_t(row0 + ar) * H + ac * 8;
-  const size_t hstride32 = size_t(32) * H;
-
-  const int kc = tid >> 5;   // 0..7
-  const int nb = tid & 31;   // 0..31
-  const uint16_t* wbase = w2 + size_t(e) * H * D + size_t(kc * 8) * D + n0 + nb * 8;
-  const bool wcol_ok = EVEN || (n0 + nb * 8 < D);
-
-  uint4 ra[8], rb[8];
-  auto load_stage = [&](int k0) {
-    const bool aok = EVEN || (k0 + ac * 8 < H);
+  TileCtx c;
+  c.ra = make_rsrc(h + size_t(row0) * H, uint32_t(BM) * H * 2);
+  const size_t wsz = size_t(H) * D;
+  c.rb = make_rsrc(w2 + size_t(e) * wsz, uint32_t(wsz * 2));
+  const int lc = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      ra[i] = aok ? *reinterpret_cast<const uint4*>(hrow + i * hstride32 + k0) : make_uint4(0, 0, 0, 0);
-    const bool kok = EVEN || (k0 + kc * 8 < H);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      rb[j] = (wcol_ok && kok) ? *reinterpret_cast<const uint4*>(wbase + size_t(k0 + j) * D)
-                               : make_uint4(0, 0, 0, 0);
-  };
-  auto store_stage = [&](uint8_t* st) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lds_store16(st, a_off(ar + 32 * i, ac), ra[i]);
-    uint4 tb[8];
-    transpose8x8(rb, tb);
-    uint8_t* sb = st + A_BYTES;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) lds_store16(sb, b_off(nb * 8 + c, kc), tb[c]);
-  };
+  for (int i = 0; i < 8; ++i) {
+    const int m = wave * 64 + i * 8 + (lane >> 3);
+    c.a_voff[i] = uint32_t(m) * uint32_t(H) * 2 + lc * 16;
+  }
+  c.a_dst = wave * 64 * 128;
+  setup_b_dma(c, lane, wave, n0 + (wave >> 1) * SUBN, D);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int sub[4] = {wn, wn, wn, wn};
+  const int cb[4] = {0, 32, 64, 96};
+  setup_reads(c, lane, wm, sub, cb);
 
   f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int wm = wave >> 1, wn = wave & 1;
-  const int a_row0 = wm * 128;
-  const int b_col[4] = {wn * 128, wn * 128 + 32, wn * 128 + 64, wn * 128 + 96};
-
-  const int ksteps = (H + BK - 1) / BK;
-  load_stage(0);
-  store_stage(smem);
-  __syncthreads();
-  for (int ks = 0; ks < ksteps; ++ks) {
-    uint8_t* cur = smem + (ks & 1) * STAGE_BYTES;
-    uint8_t* nxt = smem + ((ks + 1) & 1) * STAGE_BYTES;
-    const bool more = ks + 1 < ksteps;
-    if (more) load_stage((ks + 1) * BK);
-    mma_stage(cur, cur + A_BYTES, lane, a_row0, b_col, acc);
-    if (more) store_stage(nxt);
-    __syncthreads();
-  }
+  run_tile<EVEN>(c, (H + BK - 1) / BK, acc);
 
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = row0 + a_row0 + i * 32 + l32;
+    const int m = row0 + wm * 128 + i * 32 + l32;
     float* yrow = y + size_t(m) * D;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = n0 + b_col[j] + q * 8 + hi * 4;
+        const int col = n0 + wn * SUBN + j * 32 + q * 8 + hi * 4;
         if (!EVEN && col >= D) continue;
         f32x4 v = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
                    acc[i][j][q * 4 + 3]};
@@ -362,26 +372,26 @@ hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* e
                              const int32_t* row_slot, const uint16_t* w1, const uint16_t* w3,
                              uint16_t* h, hipStream_t stream) {
   const int mt_max = int(s.cap / BM);
-  const int nt = (s.H + 127) / 128;
+  const int nt = (s.H + SUBN - 1) / SUBN;
   const int grid = mt_max * nt;
   if (grid == 0) return hipSuccess;
-  const bool even = (s.H % 128 == 0) && (s.D % BK == 0);
+  const bool even = (s.H % SUBN == 0) && (s.D % BK == 0);
   if (even)
     hipLaunchKernelGGL(grouped_up_kernel<true>, dim3(grid), dim3(NTHR), 0, stream, x,
-                       expert_offset, row_slot, w1, w3, h, s.D, s.H, s.n, s.K);
+                       expert_offset, row_slot, w1, w3, h, s.T, s.D, s.H, s.n, s.K);
   else
     hipLaunchKernelGGL(grouped_up_kernel<false>, dim3(grid), dim3(NTHR), 0, stream, x,
-                       expert_offset, row_slot, w1, w3, h, s.D, s.H, s.n, s.K);
+                       expert_offset, row_slot, w1, w3, h, s.T, s.D, s.H, s.n, s.K);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, const uint16_t* h,
                                const uint16_t* w2, float* y_rows, hipStream_t stream) {
   const int mt_max = int(s.cap / BM);
-  const int nt = (s.D + BNC - 1) / BNC;
+  const int nt = (s.D + 2 * SUBN - 1) / (2 * SUBN);
   const int grid = mt_max * nt;
   if (grid == 0) return hipSuccess;
-  const bool even = (s.D % BNC == 0) && (s.H % BK == 0);
+  const bool even = (s.D % (2 * SUBN) == 0) && (s.H % BK == 0);
   if (even)
     hipLaunchKernelGGL(grouped_down_kernel<true>, dim3(grid), dim3(NTHR), 0, stream,
                        expert_offset, h, w2, y_rows, s.D, s.H, s.n);
