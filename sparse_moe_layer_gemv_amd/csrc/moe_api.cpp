@@ -50,10 +50,12 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
 //   topk_idx  int32 [T*K]     topk_gate fp32 [T*K]
 //   count     int32 [n]       offset    int32 [n+1]
 //   row_slot  int32 [cap]     slot_row  int32 [T*K]
-//   h         bf16  [cap][H]  y_rows    fp32  [cap][D]
+//   h         bf16  [cap][H]  y_rows    fp32  [2][cap][D] (split partials)
 struct Carve {
   size_t idx, gate, count, offset, row_slot, slot_row, h, y, total;
 };
+
+constexpr int kMaxSplits = 2;
 
 Carve carve(const Shape& s) {
   Carve c{};
@@ -66,7 +68,7 @@ Carve carve(const Shape& s) {
   c.row_slot = o; o = align_up(o + size_t(s.cap) * 4, kAlign);
   c.slot_row = o; o = align_up(o + P * 4, kAlign);
   c.h = o;        o = align_up(o + size_t(s.cap) * s.H * 2, kAlign);
-  c.y = o;        o = align_up(o + size_t(s.cap) * s.D * 4, kAlign);
+  c.y = o;        o = align_up(o + size_t(kMaxSplits) * s.cap * s.D * 4, kAlign);
   c.total = o;
   return c;
 }
@@ -79,9 +81,12 @@ bool use_decode(const Shape& s) { return s.T <= moe::kDecodeMaxTokens; }
 // after the second).
 using MarkFn = std::function<hipError_t(int)>;
 
+// Expert products into y_rows (partial 0) and, when the second product is
+// split, y_part (partial 1); returns the number of partials in *nsplit.
 moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const int32_t* offset,
                      const int32_t* row_slot, const void* w1, const void* w3, const void* w2,
-                     float* y_rows, uint16_t* h, hipStream_t st, const MarkFn& mark = nullptr) {
+                     float* y_rows, float* y_part, int* nsplit, uint16_t* h, hipStream_t st,
+                     const MarkFn& mark = nullptr) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* w1b = static_cast<const uint16_t*>(w1);
   const uint16_t* w3b = static_cast<const uint16_t*>(w3);
@@ -92,10 +97,14 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   else
     e = moe::launch_grouped_up(s, xb, offset, row_slot, w1b, w3b, h, st);
   if (e != hipSuccess || (mark && mark(3) != hipSuccess)) return MOE_EHIP;
-  if (use_decode(s))
+  *nsplit = 1;
+  if (use_decode(s)) {
     e = moe::launch_decode_down(s, count, offset, h, w2b, y_rows, st);
-  else
-    e = moe::launch_grouped_down(s, offset, h, w2b, y_rows, st);
+  } else {
+    *nsplit = y_part ? moe::grouped_down_splits(s) : 1;
+    e = moe::launch_grouped_down(s, offset, h, w2b, y_rows, *nsplit,
+                                 y_part - y_rows, st);
+  }
   if (e != hipSuccess || (mark && mark(4) != hipSuccess)) return MOE_EHIP;
   return MOE_OK;
 }
@@ -177,8 +186,14 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_
   if (!ws || ws_bytes < c.total) return MOE_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_EINVAL;
   uint8_t* base = static_cast<uint8_t*>(ws);
-  return run_ffn(s, x, expert_count, expert_offset, row_slot, w1, w3, w2, y_rows,
-                 reinterpret_cast<uint16_t*>(base + c.h), static_cast<hipStream_t>(stream));
+  float* y_part = reinterpret_cast<float*>(base + c.y);
+  int nsplit = 1;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // the split partial is written y_part - y_rows floats after y_rows
+  st = run_ffn(s, x, expert_count, expert_offset, row_slot, w1, w3, w2, y_rows, y_part, &nsplit,
+               reinterpret_cast<uint16_t*>(base + c.h), hs);
+  if (st != MOE_OK || nsplit == 1) return st;
+  return hip_status(moe::launch_add_rows(s, expert_offset, y_rows, y_part, hs));
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int32_t* slot_row,
@@ -190,7 +205,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int3
   if (!y_rows || !slot_row || !topk_gate || !out) return MOE_EINVAL;
   if (!aligned16(y_rows) || !aligned16(slot_row) || !aligned16(topk_gate) || !aligned16(out))
     return MOE_EINVAL;
-  return hip_status(moe::launch_combine(s, y_rows, slot_row, topk_gate, out,
+  return hip_status(moe::launch_combine(s, y_rows, 1, 0, slot_row, topk_gate, out,
                                         p->out_dtype == MOE_BF16,
                                         static_cast<hipStream_t>(stream)));
 }
@@ -240,10 +255,13 @@ moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void
   if (moe::launch_permute(s, idx, count, offset, row_slot, slot_row, hs) != hipSuccess ||
       mark(2) != hipSuccess)
     return MOE_EHIP;
-  st = run_ffn(s, x, count, offset, row_slot, w1, w3, w2, y, h, hs,
+  const size_t part_stride = size_t(s.cap) * s.D;
+  int nsplit = 1;
+  st = run_ffn(s, x, count, offset, row_slot, w1, w3, w2, y, y + part_stride, &nsplit, h, hs,
                events ? MarkFn(mark) : MarkFn());
   if (st != MOE_OK) return st;
-  if (moe::launch_combine(s, y, slot_row, gate, out, p->out_dtype == MOE_BF16, hs) != hipSuccess ||
+  if (moe::launch_combine(s, y, nsplit, part_stride, slot_row, gate, out,
+                          p->out_dtype == MOE_BF16, hs) != hipSuccess ||
       mark(5) != hipSuccess)
     return MOE_EHIP;
   return MOE_OK;

@@ -14,8 +14,9 @@ constexpr int kCombineThreads = 256;
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const float* __restrict__ y_rows, const int32_t* __restrict__ slot_row,
-    const float* __restrict__ gate, int D, int K, void* __restrict__ out) {
+    const float* __restrict__ y_rows, int nsplit, size_t split_stride,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ gate, int D, int K,
+    void* __restrict__ out) {
   const int t = blockIdx.x;
   for (int d = threadIdx.x * 4; d < D; d += kCombineThreads * 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -23,7 +24,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       const int r = slot_row[size_t(t) * K + k];
       if (r < 0) continue;
       const float g = gate[size_t(t) * K + k];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(y_rows + size_t(r) * D + d);
+      f32x4 v = *reinterpret_cast<const f32x4*>(y_rows + size_t(r) * D + d);
+      for (int p = 1; p < nsplit; ++p)
+        v += *reinterpret_cast<const f32x4*>(y_rows + p * split_stride + size_t(r) * D + d);
       acc[0] = fmaf(g, v[0], acc[0]);
       acc[1] = fmaf(g, v[1], acc[1]);
       acc[2] = fmaf(g, v[2], acc[2]);
@@ -42,15 +45,37 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
 }  // namespace
 
-hipError_t launch_combine(const Shape& s, const float* y_rows, const int32_t* slot_row,
-                          const float* topk_gate, void* out, bool out_bf16, hipStream_t stream) {
+hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_t split_stride,
+                          const int32_t* slot_row, const float* topk_gate, void* out,
+                          bool out_bf16, hipStream_t stream) {
   if (s.T == 0) return hipSuccess;
   if (out_bf16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(s.T), dim3(kCombineThreads), 0, stream, y_rows,
-                       slot_row, topk_gate, s.D, s.K, out);
+                       nsplit, split_stride, slot_row, topk_gate, s.D, s.K, out);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(s.T), dim3(kCombineThreads), 0, stream, y_rows,
-                       slot_row, topk_gate, s.D, s.K, out);
+                       nsplit, split_stride, slot_row, topk_gate, s.D, s.K, out);
+  return hipGetLastError();
+}
+
+// Sum of the split partial products for callers of the stage API that want
+// whole rows: y_rows[r] += y_part[r] over the rows of the expert segments.
+__global__ __launch_bounds__(kCombineThreads) void add_rows_kernel(
+    const int32_t* __restrict__ expert_offset, int n, int D, float* __restrict__ y,
+    const float* __restrict__ y_part) {
+  const size_t total = size_t(expert_offset[n]) * D / 4;
+  for (size_t i = size_t(blockIdx.x) * kCombineThreads + threadIdx.x; i < total;
+       i += size_t(gridDim.x) * kCombineThreads) {
+    f32x4 a = reinterpret_cast<f32x4*>(y)[i];
+    a += reinterpret_cast<const f32x4*>(y_part)[i];
+    reinterpret_cast<f32x4*>(y)[i] = a;
+  }
+}
+
+hipError_t launch_add_rows(const Shape& s, const int32_t* expert_offset, float* y_rows,
+                           const float* y_part, hipStream_t stream) {
+  hipLaunchKernelGGL(add_rows_kernel, dim3(1024), dim3(kCombineThreads), 0, stream, expert_offset,
+                     s.n, s.D, y_rows, y_part);
   return hipGetLastError();
 }
 

@@ -181,6 +181,7 @@ struct TileCtx {
   int a_dst, b_dst;               // wave's LDS destination offsets within a stage
   uint32_t x_rd[4];               // activation fragment read offsets, per 16-deep slice
   uint32_t w_rd[4];               // weight fragment read offsets, per fragment j
+  int kbase;                      // first contraction element of this tile's range
 };
 
 // DMA of the activation rows for contraction elements [k0, k0 + 64);
@@ -188,7 +189,8 @@ struct TileCtx {
 template <int I0 = 0, int I1 = A_DMA>
 __device__ __forceinline__ void issue_a(const TileCtx& c, uint8_t* st, int k0) {
 #pragma unroll
-  for (int i = I0; i < I1; ++i) dma16(c.ra, lds(st) + c.a_dst + i * 8 * 128, c.a_voff[i], k0 * 2);
+  for (int i = I0; i < I1; ++i)
+    dma16(c.ra, lds(st) + c.a_dst + i * 8 * 128, c.a_voff[i], uint32_t(c.kbase + k0) * 2);
 }
 
 // DMA of both weight sub-tiles for contraction rows [k0, k0 + 32).
@@ -196,7 +198,7 @@ template <bool EVEN>
 __device__ __forceinline__ void issue_b(const TileCtx& c, uint8_t* st, int k0) {
 #pragma unroll
   for (int i = 0; i < B_DMA; ++i) {
-    const uint32_t rows = uint32_t(k0 + i * 4) * c.b_row_bytes;
+    const uint32_t rows = uint32_t(c.kbase + k0 + i * 4) * c.b_row_bytes;
     if (EVEN)
       dma16(c.rb, lds(st) + c.b_dst + i * 4 * SUBN * 2, c.b_voff, rows);
     else
@@ -442,6 +444,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   TileCtx c;
+  c.kbase = 0;
   c.ra = make_rsrc(x, uint32_t(T) * D * 2);
   const size_t wsz = size_t(D) * H;
   c.rb = make_rsrc(((wave >> 1) ? w3 : w1) + size_t(e) * wsz, uint32_t(wsz * 2));
@@ -497,22 +500,31 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
 // ---------------------------------------------------------------------------
 // down: y = h w2
 // ---------------------------------------------------------------------------
+// The contraction (H) can be split into `nsplit` ranges of `klen` elements;
+// split ks writes its partial product to y + ks * split_stride, and the
+// partials are added (in split order) by the consumer.  This evens out the
+// last round of workgroups when the tile count is not a multiple of the CUs.
 template <bool EVEN>
 __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
     const int32_t* __restrict__ expert_offset, const uint16_t* __restrict__ h,
-    const uint16_t* __restrict__ w2, float* __restrict__ y, int D, int H, int n) {
+    const uint16_t* __restrict__ w2, float* __restrict__ y, int D, int H, int n, int nsplit,
+    int klen, ptrdiff_t split_stride) {
   const int mt_count = expert_offset[n] / BM;
   const int nt_count = (D + 2 * SUBN - 1) / (2 * SUBN);
-  int mt, nt;
-  if (!map_tile(blockIdx.x, mt_count, nt_count, mt, nt)) return;
+  int mt, unit;
+  if (!map_tile(blockIdx.x, mt_count, nt_count * nsplit, mt, unit)) return;
+  const int nt = unit / nsplit;
+  const int ks = unit - nt * nsplit;
   const int row0 = mt * BM;
   const int e = expert_of_row(expert_offset, n, row0);
   const int n0 = nt * 2 * SUBN;
+  y += ks * split_stride;  // may point into another allocation (the workspace)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   TileCtx c;
+  c.kbase = ks * klen;
   c.ra = make_rsrc(h + size_t(row0) * H, uint32_t(BM) * H * 2);
   const size_t wsz = size_t(H) * D;
   c.rb = make_rsrc(w2 + size_t(e) * wsz, uint32_t(wsz * 2));
@@ -527,7 +539,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
   setup_reads(c, lane, wm, sub, cb);
 
   f32x16 acc[4][4];
-  run_tile<EVEN, !EVEN>(c, (H + BK - 1) / BK, acc);
+  run_tile<EVEN, !EVEN>(c, (min(klen, H - c.kbase) + BK - 1) / BK, acc);
 
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -568,19 +580,27 @@ hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* e
   return hipGetLastError();
 }
 
+int grouped_down_splits(const Shape& s) {
+  const int klen = s.H / 2;
+  return (s.H % (2 * 4 * BK) == 0 && klen >= 8 * BK && s.D % (2 * SUBN) == 0) ? 2 : 1;
+}
+
 hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, const uint16_t* h,
-                               const uint16_t* w2, float* y_rows, hipStream_t stream) {
+                               const uint16_t* w2, float* y_rows, int nsplit, ptrdiff_t split_stride,
+                               hipStream_t stream) {
   const int mt_max = int(s.cap / BM);
   const int nt = (s.D + 2 * SUBN - 1) / (2 * SUBN);
-  const int grid = mt_max * nt;
+  const int grid = mt_max * nt * nsplit;
   if (grid == 0) return hipSuccess;
-  const bool even = (s.D % (2 * SUBN) == 0) && (s.H % (4 * BK) == 0) && s.H >= 8 * BK;
+  const int klen = s.H / nsplit;
+  const bool even = (s.D % (2 * SUBN) == 0) && (klen % (4 * BK) == 0) && klen >= 8 * BK &&
+                    klen * nsplit == s.H;
   if (even)
     hipLaunchKernelGGL(grouped_down_kernel<true>, dim3(grid), dim3(NTHR), 0, stream,
-                       expert_offset, h, w2, y_rows, s.D, s.H, s.n);
+                       expert_offset, h, w2, y_rows, s.D, s.H, s.n, nsplit, klen, split_stride);
   else
     hipLaunchKernelGGL(grouped_down_kernel<false>, dim3(grid), dim3(NTHR), 0, stream,
-                       expert_offset, h, w2, y_rows, s.D, s.H, s.n);
+                       expert_offset, h, w2, y_rows, s.D, s.H, s.n, 1, s.H, split_stride);
   return hipGetLastError();
 }
 

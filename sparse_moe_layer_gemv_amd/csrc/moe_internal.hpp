@@ -34,8 +34,13 @@ hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* expe
 hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_offset,
                              const int32_t* row_slot, const uint16_t* w1, const uint16_t* w3,
                              uint16_t* h, hipStream_t stream);
+// The second product may be split along its contraction into `nsplit`
+// partial sums: partial ks at y_rows + ks * split_stride (see
+// grouped_down_splits).
+int grouped_down_splits(const Shape& s);
 hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, const uint16_t* h,
-                               const uint16_t* w2, float* y_rows, hipStream_t stream);
+                               const uint16_t* w2, float* y_rows, int nsplit, ptrdiff_t split_stride,
+                               hipStream_t stream);
 
 // Weight-streaming path for small T (every touched expert's weights read once).
 hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
@@ -46,7 +51,14 @@ hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
                               const int32_t* expert_offset, const uint16_t* h,
                               const uint16_t* w2, float* y_rows, hipStream_t stream);
 
-hipError_t launch_combine(const Shape& s, const float* y_rows, const int32_t* slot_row,
-                          const float* topk_gate, void* out, bool out_bf16, hipStream_t stream);
+// out[t] = sum_k gate[t][k] * (sum_p y_rows[p * split_stride + row(t,k)]),
+// partials p summed first, in order.
+hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_t split_stride,
+                          const int32_t* slot_row, const float* topk_gate, void* out,
+                          bool out_bf16, hipStream_t stream);
+
+// y_rows[r] += y_part[r] for the rows of the expert segments (r < offset[n]).
+hipError_t launch_add_rows(const Shape& s, const int32_t* expert_offset, float* y_rows,
+                           const float* y_part, hipStream_t stream);
 
 }  // namespace moe

@@ -111,10 +111,13 @@ def test_permute_drops_out_of_range_experts(moe):
 
 
 FORCED = [
-    # label, forced expert choice per token (K=2), T
-    ("all_on_expert3", lambda T: np.tile([[3, 5]], (T, 1)), 700),
-    ("counts_255_256_257", None, 0),
-    ("one_expert_k1", lambda T: np.full((T, 1), 6), 600),
+    # label, forced expert choice per token, T, D, H
+    ("all_on_expert3", lambda T: np.tile([[3, 5]], (T, 1)), 700, 256, 384),
+    ("counts_255_256_257", None, 0, 256, 384),
+    ("one_expert_k1", lambda T: np.full((T, 1), 6), 600, 256, 384),
+    # H = 1024: the second product runs as two contraction halves whose
+    # partial sums are added before returning y_rows
+    ("split_contraction", lambda T: np.stack([np.arange(T) % 8, (np.arange(T) + 3) % 8], 1), 900, 512, 1024),
 ]
 
 
@@ -123,12 +126,12 @@ def _forced_counts_case():
     return np.concatenate([np.zeros(255), np.ones(256), np.full(257, 2)]).astype(np.int32)[:, None]
 
 
-@pytest.mark.parametrize("label,make,T", FORCED, ids=[f[0] for f in FORCED])
-def test_grouped_ffn_forced_routing(moe, label, make, T):
+@pytest.mark.parametrize("label,make,T,D,H", FORCED, ids=[f[0] for f in FORCED])
+def test_grouped_ffn_forced_routing(moe, label, make, T, D, H):
     import torch
     idx = _forced_counts_case() if make is None else np.asarray(make(T), np.int32)
     T, K = idx.shape
-    D, H, n = 256, 384, 8
+    n = 8
     L = moe_synth.make_layer(T, D, H, n, K, seed=41)
     d = _upload(L)
     perm = moe.permute(dev_i32(idx), n)
