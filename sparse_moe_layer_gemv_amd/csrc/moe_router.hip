@@ -3,14 +3,17 @@
 // is the softmax of the Top-K logits of a linear layer; logits outside the
 // top K are set to -inf, so they get a gate of exactly zero.
 //
-// One wavefront owns TPW consecutive tokens.  Each lane walks the dim axis in
-// 8-element (16-byte) steps strided by 512, so a wave reads each token row as
-// fully coalesced 1 KiB segments; the router row W_g[k][0..n) is loaded once
-// per step and reused for all TPW tokens.  The n partial sums per token are
-// reduced across the wave with a butterfly, then lane t picks the top K of
-// token t in registers (strict ">" so the lower expert index wins a tie) and
-// writes the softmax over the kept logits.  The kernel is bound by reading x
-// from HBM (n = 8 multiply-adds per 2-byte element).
+// A workgroup of 4 wavefronts owns TPW consecutive tokens and splits the dim
+// axis between its waves: lane l of wave w reads the 16-byte steps
+// 8*(64*w + l) + 2048*i, so each token row is read as coalesced 1 KiB
+// segments, and every W_g row is loaded once per step and reused for the TPW
+// tokens.  The n partial sums per token are reduced across each wave with a
+// butterfly and across the 4 waves through LDS in a fixed order; then lane t
+// of wave 0 picks the top K of token t in registers (strict ">" so the lower
+// expert index wins a tie) and writes the softmax over the kept logits.
+// The kernel is bound by reading x from HBM (n = 8 multiply-adds per 2-byte
+// element); splitting the dim axis over 4 waves keeps small batches (decode)
+// from being one long dependent chain of loads.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -25,10 +28,11 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T, int D, int n,
     int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
     float* __restrict__ logits) {
+  constexpr int kWaves = kRouterThreads / 64;
+  __shared__ float red[kWaves][TPW][NE];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t0 = (blockIdx.x * (kRouterThreads / 64) + wave) * TPW;
-  if (t0 >= T) return;
+  const int t0 = blockIdx.x * TPW;
 
   float acc[TPW][NE];
 #pragma unroll
@@ -36,7 +40,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[t][e] = 0.f;
 
-  for (int k = lane * 8; k < D; k += 512) {
+  for (int k = (wave * 64 + lane) * 8; k < D; k += kRouterThreads * 8) {
     uint4 xv[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -76,16 +80,29 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[t][e] = wave_sum(acc[t][e]);
+    for (int e = 0; e < NE; ++e) {
+      const float v = wave_sum(acc[t][e]);
+      if (lane == 0) red[wave][t][e] = v;
+    }
+  __syncthreads();
+  if (wave != 0) return;
 
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int tok = t0 + t;
     if (lane != t || tok >= T) continue;
+    float l[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      float v = red[0][t][e];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v += red[w][t][e];
+      l[e] = v;
+    }
     if (logits) {
 #pragma unroll
       for (int e = 0; e < NE; ++e)
-        if (e < n) logits[size_t(tok) * n + e] = acc[t][e];
+        if (e < n) logits[size_t(tok) * n + e] = l[e];
     }
     // Top-K by repeated selection: strictly larger wins, so ties keep the
     // lower index, and slot order is decreasing logit.
@@ -101,9 +118,9 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
         float bv = 0.f;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-          if (e < n && !((taken >> e) & 1ull) && (bi < 0 || acc[t][e] > bv)) {
+          if (e < n && !((taken >> e) & 1ull) && (bi < 0 || l[e] > bv)) {
             bi = e;
-            bv = acc[t][e];
+            bv = l[e];
           }
         }
         taken |= 1ull << bi;
@@ -133,8 +150,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 template <int NE, int TPW, bool VEC>
 hipError_t launch_router_t(const Shape& s, const uint16_t* x, const uint16_t* wg, int32_t* idx,
                            float* gate, float* logits, hipStream_t stream) {
-  const int tokens_per_block = (kRouterThreads / 64) * TPW;
-  const int blocks = (s.T + tokens_per_block - 1) / tokens_per_block;
+  const int blocks = (s.T + TPW - 1) / TPW;
   hipLaunchKernelGGL((router_kernel<NE, TPW, VEC>), dim3(blocks), dim3(kRouterThreads), 0,
                      stream, x, wg, s.T, s.D, s.n, s.K, idx, gate, logits);
   return hipGetLastError();
