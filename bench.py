@@ -161,6 +161,7 @@ def main(argv=None):
 
     import torch
     import sparse_moe_layer_gemv_amd as moe
+    from sparse_moe_layer_gemv_amd.profiling import load_traffic
 
     w = moe_synth.WORKLOADS[args.workload]
     T, D, H, n, K = w.T, w.D, w.H, w.n, w.K
@@ -218,19 +219,24 @@ def main(argv=None):
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=n)
     touched = int((counts > 0).sum())
     decode = T <= moe.decode_max_tokens()
+    kernel = "decode_up" if decode else "grouped_up"
+    # HBM bytes per launch from the stored counter runs of this exact kernel
+    # source (None once the source has changed since they were taken)
+    tr = load_traffic(kernel, args.workload)
+    traffic = None if tr is None else tr["bytes_per_launch"]
     if decode:
         # the weight-streaming kernel reads w1 and w3 of every touched expert once
         per_launch = up_weight_bytes(touched, D, H)
         achieved = per_launch / (stage_avg["up"] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "decode_up",
-                "algorithmic_per_launch": per_launch}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": kernel,
+                "algorithmic_per_launch": per_launch, "traffic_unit": "HBM bytes per launch"}
     else:
         per_launch = up_flops(chunk, D, H, K)
         achieved = per_launch / (stage_avg["up"] / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "grouped_up",
-                "algorithmic_per_launch": per_launch}
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kernel,
+                "algorithmic_per_launch": per_launch, "traffic_unit": "HBM bytes per launch"}
 
     rec = {
         "metric": METRIC,

@@ -40,9 +40,9 @@
 //
 // Workgroup order: the hardware hands workgroup ids to the 8 XCDs round-robin,
 // and each XCD has its own L2.  The block id is remapped so every XCD works on
-// a contiguous range of tiles, and tiles are rastered in groups of 4 row-tiles
-// so the ~32 workgroups resident on one XCD share 4 activation panels and 8
-// weight panels in its L2.
+// a contiguous range of tiles ordered expert by expert, with an expert's
+// row-tiles consecutive, so the workgroups resident on one XCD share each
+// weight panel and a few activation panels in its L2.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -66,7 +66,6 @@ constexpr int NB = 4;                       // weight stages: DMA 3 steps ahead
 constexpr int NA = 2;                       // activation stages (2 steps each)
 constexpr int A_DMA = 8;                    // activation DMA instructions per wave per A stage
 constexpr int B_DMA = 4;                    // weight DMA instructions per wave per step
-constexpr int GROUP_M = 4;
 constexpr uint32_t kOOB = 0x80000000u;      // buffer offset beyond any resource (< 2^31 bytes): reads as 0
 constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data (gfx9 family)
 
@@ -137,23 +136,38 @@ __device__ __forceinline__ bf16x8 lds_read_wfrag(uint8_t* base, uint32_t off) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// XCD-aware tile mapping.  Workgroup L runs on XCD L % 8.  Valid workgroups
-// (L < total) are renumbered so XCD x gets a contiguous range, then the range
-// is rastered in groups of GROUP_M row-tiles with the row index fastest.
-__device__ __forceinline__ bool map_tile(int L, int mt_count, int nt_count, int& mt, int& nt) {
-  const int total = mt_count * nt_count;
+// XCD-aware, expert-grouped tile mapping.  The hardware hands workgroup ids to
+// the 8 XCDs round-robin (workgroup L runs on XCD L % 8) and each XCD has its
+// own L2.  Valid workgroups (L < total tiles) are renumbered so that XCD x
+// gets a contiguous range v of a linear tile order, and that order walks the
+// experts one after the other; within an expert, column-tile by column-tile,
+// with all of the expert's row-tiles consecutive.  So the workgroups resident
+// on one XCD at a time work on one expert and share each weight panel (read
+// once into that L2) and a few activation panels.
+//   offset: segment starts (tile-aligned), n experts, nu: column units per row
+//   tile.  Returns false for workgroups beyond the valid tiles.
+__device__ __forceinline__ bool map_tile(int L, const int32_t* __restrict__ offset, int n,
+                                         int nu, int& mt, int& unit) {
+  const int mt_count = offset[n] / BM;
+  const int total = mt_count * nu;
   if (L >= total) return false;
   const int xcd = L & 7;
   const int local = L >> 3;
   const int q = total >> 3, rem = total & 7;
-  const int v = xcd * q + min(xcd, rem) + local;
-  const int group = GROUP_M * nt_count;
-  const int g = v / group;
-  const int r = v - g * group;
-  const int rows_in_group = min(GROUP_M, mt_count - g * GROUP_M);
-  mt = g * GROUP_M + r % rows_in_group;
-  nt = r / rows_in_group;
-  return true;
+  int v = xcd * q + min(xcd, rem) + local;
+  // expert of linear tile v
+  int e = 0, m0 = 0;
+  for (; e < n; ++e) {
+    const int me = (offset[e + 1] - offset[e]) / BM;
+    if (v < me * nu) {
+      mt = m0 + v % me;
+      unit = v / me;
+      return true;
+    }
+    v -= me * nu;
+    m0 += me;
+  }
+  return false;  // not reached: v < total
 }
 
 // Expert owning permuted row `row0` (segments are tile-aligned).
@@ -432,10 +446,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
     const int32_t* __restrict__ row_slot, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ w3, uint16_t* __restrict__ h, int T, int D, int H, int n, int K,
     int k_shift) {
-  const int mt_count = expert_offset[n] / BM;
   const int nt_count = (H + SUBN - 1) / SUBN;
   int mt, nt;
-  if (!map_tile(blockIdx.x, mt_count, nt_count, mt, nt)) return;
+  if (!map_tile(blockIdx.x, expert_offset, n, nt_count, mt, nt)) return;
   const int row0 = mt * BM;
   const int e = expert_of_row(expert_offset, n, row0);
   const int n0 = nt * SUBN;
@@ -509,10 +522,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
     const int32_t* __restrict__ expert_offset, const uint16_t* __restrict__ h,
     const uint16_t* __restrict__ w2, float* __restrict__ y, int D, int H, int n, int nsplit,
     int klen, ptrdiff_t split_stride) {
-  const int mt_count = expert_offset[n] / BM;
   const int nt_count = (D + 2 * SUBN - 1) / (2 * SUBN);
   int mt, unit;
-  if (!map_tile(blockIdx.x, mt_count, nt_count * nsplit, mt, unit)) return;
+  if (!map_tile(blockIdx.x, expert_offset, n, nt_count * nsplit, mt, unit)) return;
   const int nt = unit / nsplit;
   const int ks = unit - nt * nsplit;
   const int row0 = mt * BM;
