@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <functional>
 
 #include "moe_internal.hpp"
@@ -51,6 +52,8 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
 //   count     int32 [n]       offset    int32 [n+1]
 //   row_slot  int32 [cap]     slot_row  int32 [T*K]
 //   h         bf16  [cap][H]  y_rows    fp32  [2][cap][D] (split partials)
+// With the weight-streaming path (T <= kDecodeMaxTokens) the h region holds
+// the fp32 first-product results instead (decode_scratch_bytes).
 struct Carve {
   size_t idx, gate, count, offset, row_slot, slot_row, h, y, total;
 };
@@ -67,7 +70,9 @@ Carve carve(const Shape& s) {
   c.offset = o;   o = align_up(o + size_t(s.n + 1) * 4, kAlign);
   c.row_slot = o; o = align_up(o + size_t(s.cap) * 4, kAlign);
   c.slot_row = o; o = align_up(o + P * 4, kAlign);
-  c.h = o;        o = align_up(o + size_t(s.cap) * s.H * 2, kAlign);
+  size_t h_bytes = size_t(s.cap) * s.H * 2;
+  if (s.T <= moe::kDecodeMaxTokens) h_bytes = std::max(h_bytes, moe::decode_scratch_bytes(s));
+  c.h = o;        o = align_up(o + h_bytes, kAlign);
   c.y = o;        o = align_up(o + size_t(kMaxSplits) * s.cap * s.D * 4, kAlign);
   c.total = o;
   return c;
@@ -92,14 +97,17 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   const uint16_t* w3b = static_cast<const uint16_t*>(w3);
   const uint16_t* w2b = static_cast<const uint16_t*>(w2);
   hipError_t e;
+  float* ab = reinterpret_cast<float*>(h);  // decode: fp32 first products
   if (use_decode(s))
-    e = moe::launch_decode_up(s, xb, count, offset, row_slot, w1b, w3b, h, st);
+    e = moe::launch_decode_up(s, xb, count, offset, row_slot, w1b, w3b, ab, st);
   else
     e = moe::launch_grouped_up(s, xb, offset, row_slot, w1b, w3b, h, st);
   if (e != hipSuccess || (mark && mark(3) != hipSuccess)) return MOE_EHIP;
   *nsplit = 1;
   if (use_decode(s)) {
-    e = moe::launch_decode_down(s, count, offset, h, w2b, y_rows, st);
+    *nsplit = y_part ? moe::decode_down_splits(s) : 1;
+    e = moe::launch_decode_down(s, count, offset, row_slot, ab, w2b, y_rows, *nsplit,
+                                y_part - y_rows, st);
   } else {
     *nsplit = y_part ? moe::grouped_down_splits(s) : 1;
     e = moe::launch_grouped_down(s, offset, h, w2b, y_rows, *nsplit,

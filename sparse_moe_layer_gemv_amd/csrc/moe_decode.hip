@@ -6,18 +6,23 @@
 // T <= 32 tokens each expert sees only a handful of rows, so the expert
 // products are bound by reading the weights: every touched expert's w1, w3
 // and w2 must cross HBM once and nothing else matters.  These kernels do
-// exactly that read, once, coalesced, with enough loads in flight to keep HBM
-// busy, and use the matrix cores only to keep the arithmetic off the critical
-// path.
+// exactly that read, once, coalesced, with many loads in flight, and use the
+// matrix cores only to keep the arithmetic off the critical path.
 //
-// Work split: a workgroup owns (expert e, 128 output columns); its waves split
-// the contraction axis.  Per 32-wide step a lane loads an 8 x 8 bf16 block of
-// each weight matrix (8 rows x 16 bytes; 16 lanes cover 256 contiguous bytes
-// of a row), transposes it in registers, and feeds 8 v_mfma_f32_16x16x32_bf16
-// whose A rows are 16 hidden units strided by 8 columns and whose B columns
-// are up to 16 token rows of the expert.  The waves' partial sums are reduced
-// through LDS in a fixed tree order (deterministic), and wave 0 applies the
-// epilogue: silu(a)*b -> bf16 h for the up products, fp32 y for the down ones.
+// Work split: a workgroup owns (expert e, 128 output columns, one weight
+// matrix); its waves split the contraction axis.  Per 32-wide step a lane
+// loads an 8 x 8 bf16 block of the matrix (8 rows x 16 bytes; 16 lanes cover
+// 256 contiguous bytes of a row), transposes it in registers, and feeds 8
+// v_mfma_f32_16x16x32_bf16 whose A rows are 16 output columns strided by 8
+// and whose B columns are up to 16 token rows of the expert.  The waves'
+// partial sums are reduced through LDS in a fixed tree order (deterministic).
+//
+// First product: w1 and w3 are separate workgroups (twice as many workgroups
+// keep more loads in flight than one workgroup reading both), each writing its
+// fp32 result a = x.w1 or b = x.w3 per token-slot.  Second product: each lane
+// forms its h fragment as bf16(silu(a) * b) while loading it (the same single
+// rounding as the tiled path), and the 14336-deep contraction is split into
+// partial sums written to separate buffers, added in order by the combine.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -46,23 +51,38 @@ __device__ __forceinline__ void transpose8x8_d(const uint4 (&in)[8], uint4 (&out
   }
 }
 
-// UP:   act = x [T][Kdim], rows gathered through row_slot; wa = w1, wb = w3;
-//       out = h bf16 [cap][Ndim]
-// DOWN: act = h [cap][Kdim], rows are the expert's permuted rows; wa = w2;
-//       out = y fp32 [cap][Ndim]
+// 8 consecutive h values of one token-slot: bf16(silu(a) * b) from the fp32
+// first-product results.
+__device__ __forceinline__ uint4 h_fragment(const float* a, const float* b) {
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(a), a1 = *reinterpret_cast<const f32x4*>(a + 4);
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 4);
+  return make_uint4(pack_bf16x2(silu(a0[0]) * b0[0], silu(a0[1]) * b0[1]),
+                    pack_bf16x2(silu(a0[2]) * b0[2], silu(a0[3]) * b0[3]),
+                    pack_bf16x2(silu(a1[0]) * b1[0], silu(a1[1]) * b1[1]),
+                    pack_bf16x2(silu(a1[2]) * b1[2], silu(a1[3]) * b1[3]));
+}
+
+// UP:   x [T][Kdim] bf16 rows gathered through row_slot; w = w1 or w3 (by
+//       workgroup); out = ab fp32 [2][P][Ndim] (a at [0], b at [1], row = slot)
+// DOWN: ab rows through row_slot -> h; w = w2; out = y fp32 [cap][Ndim] + ks *
+//       split_stride (partial ks over contraction rows [ks*klen, +klen))
 template <bool UP, int RG, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
-    const uint16_t* __restrict__ act, const int32_t* __restrict__ expert_count,
-    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ row_slot,
-    const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, void* __restrict__ out,
-    int Kdim, int Ndim, int topk, int ncb) {
-  constexpr int NMAT = UP ? 2 : 1;
-  constexpr int NACC = NMAT * RG * 8;             // f32x4 accumulators per lane
+    const uint16_t* __restrict__ x, const float* __restrict__ ab,
+    const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
+    const int32_t* __restrict__ row_slot, const uint16_t* __restrict__ w0,
+    const uint16_t* __restrict__ w1, void* __restrict__ out, int Kdim, int Ndim, int topk,
+    int P, int ncb, int nsplit, int klen, ptrdiff_t split_stride) {
+  constexpr int NACC = RG * 8;                     // f32x4 accumulators per lane
   constexpr int RED_SLOTS = WAVES / 2;
   __shared__ float red[RED_SLOTS * NACC * 4 * 64];
 
-  const int e = blockIdx.x / ncb;
-  const int cb = blockIdx.x - e * ncb;
+  // workgroup -> (expert, column block, matrix or contraction split)
+  const int per_e = ncb * (UP ? 2 : nsplit);
+  const int e = blockIdx.x / per_e;
+  const int r = blockIdx.x - e * per_e;
+  const int sub = UP ? (r & 1) : (r % nsplit);     // UP: matrix; DOWN: split
+  const int cb = UP ? (r >> 1) : (r / nsplit);
   const int cnt = expert_count[e];
   if (cnt == 0) return;
   const int rbase = expert_offset[e];
@@ -72,63 +92,67 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   const int kg = lane >> 4;
   const int nbk = lane & 15;
   const bool col_ok = n0 + nbk * 8 < Ndim;
+  const int kbeg = UP ? 0 : sub * klen;
+  const int kend = UP ? Kdim : min(Kdim, kbeg + klen);
 
-  const uint16_t* arow[RG];
+  // activation row pointers (token row j = lane % 16 + 16 g of the expert)
+  const uint16_t* xrow[RG];
+  const float* arow[RG];
+  const float* brow[RG];
   bool aval[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     const int j = (lane & 15) + 16 * g;
     aval[g] = j < cnt;
+    const int slot = aval[g] ? row_slot[rbase + j] : 0;
+    const int sl = slot >= 0 ? slot : 0;
     if (UP) {
-      const int slot = aval[g] ? row_slot[rbase + j] : 0;
-      arow[g] = act + size_t(slot >= 0 ? slot / topk : 0) * Kdim;
+      xrow[g] = x + size_t(sl / topk) * Kdim;
     } else {
-      arow[g] = act + size_t(rbase + (aval[g] ? j : 0)) * Kdim;
+      arow[g] = ab + size_t(sl) * Kdim;
+      brow[g] = ab + (size_t(P) + sl) * Kdim;
     }
   }
-  const size_t wstride = size_t(Kdim) * Ndim;
-  const uint16_t* wp[NMAT];
-  wp[0] = wa + size_t(e) * wstride + n0 + nbk * 8;
-  if (UP) wp[NMAT - 1] = wb + size_t(e) * wstride + n0 + nbk * 8;
+  const uint16_t* wp =
+      (UP && sub ? w1 : w0) + size_t(e) * Kdim * Ndim + n0 + nbk * 8;
 
-  f32x4 acc[NMAT][RG][8];
+  f32x4 acc[RG][8];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+  for (int g = 0; g < RG; ++g)
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[m][g][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 8; ++c) acc[g][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int steps = (Kdim + 31) / 32;
+  const int steps = (kend - kbeg + 31) / 32;
   const int per = (steps + WAVES - 1) / WAVES;
   const int s0 = wave * per;
   const int s1 = min(steps, s0 + per);
   for (int s = s0; s < s1; ++s) {
-    const int kk = s * 32 + kg * 8;
-    const bool kok = kk < Kdim;
-    uint4 wv[NMAT][8];
+    const int kk = kbeg + s * 32 + kg * 8;
+    const bool kok = kk < kend;
+    uint4 wv[8];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        wv[m][j] = (kok && col_ok) ? *reinterpret_cast<const uint4*>(wp[m] + size_t(kk + j) * Ndim)
-                                   : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 8; ++j)
+      wv[j] = (kok && col_ok) ? *reinterpret_cast<const uint4*>(wp + size_t(kk + j) * Ndim)
+                              : make_uint4(0, 0, 0, 0);
     bf16x8 xv[RG];
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
-      xv[g] = as_bf16x8((kok && aval[g]) ? *reinterpret_cast<const uint4*>(arow[g] + kk)
-                                         : make_uint4(0, 0, 0, 0));
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      uint4 op[8];
-      transpose8x8_d(wv[m], op);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int g = 0; g < RG; ++g)
-          acc[m][g][c] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op[c]), xv[g], acc[m][g][c], 0, 0, 0);
+    for (int g = 0; g < RG; ++g) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kok && aval[g]) {
+        if (UP)
+          v = *reinterpret_cast<const uint4*>(xrow[g] + kk);
+        else
+          v = h_fragment(arow[g] + kk, brow[g] + kk);
+      }
+      xv[g] = as_bf16x8(v);
     }
+    uint4 op[8];
+    transpose8x8_d(wv, op);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        acc[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op[c]), xv[g], acc[g][c], 0, 0, 0);
   }
 
   // Tree reduction over waves: at each level the upper half stores, the lower
@@ -139,91 +163,93 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
       float* dst = red + size_t(wave - half) * NACC * 4 * 64;
       int v = 0;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+      for (int g = 0; g < RG; ++g)
 #pragma unroll
-        for (int g = 0; g < RG; ++g)
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-          for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int r = 0; r < 4; ++r, ++v) dst[v * 64 + lane] = acc[m][g][c][r];
+          for (int q = 0; q < 4; ++q, ++v) dst[v * 64 + lane] = acc[g][c][q];
     }
     __syncthreads();
     if (wave < half) {
       const float* src = red + size_t(wave) * NACC * 4 * 64;
       int v = 0;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+      for (int g = 0; g < RG; ++g)
 #pragma unroll
-        for (int g = 0; g < RG; ++g)
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-          for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int r = 0; r < 4; ++r, ++v) acc[m][g][c][r] += src[v * 64 + lane];
+          for (int q = 0; q < 4; ++q, ++v) acc[g][c][q] += src[v * 64 + lane];
     }
     __syncthreads();
   }
-  if (wave != 0 || !col_ok) return;
+  if (wave != 0) return;
 
-  // Lane holds token row (lane & 15) + 16 g and, for register r, the 8
-  // consecutive output columns n0 + (4 (lane >> 4) + r) * 8 + c, c = 0..7.
+  // Lane holds token row (lane & 15) + 16 g and, for register q, the 8
+  // consecutive output columns n0 + (4 (lane >> 4) + q) * 8 + c, c = 0..7.
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     if (!aval[g]) continue;
-    const size_t row = size_t(rbase + (lane & 15) + 16 * g);
+    const int j = (lane & 15) + 16 * g;
+    const size_t orow = UP ? size_t(sub) * P + row_slot[rbase + j] : size_t(rbase + j);
+    float* op = static_cast<float*>(out) + (UP ? 0 : sub * split_stride) + orow * Ndim;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int col = n0 + (4 * (lane >> 4) + r) * 8;
+    for (int q = 0; q < 4; ++q) {
+      const int col = n0 + (4 * (lane >> 4) + q) * 8;
       if (col >= Ndim) continue;
-      if constexpr (UP) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int c = 0; c < 8; c += 2)
-          pk[c / 2] = pack_bf16x2(silu(acc[0][g][c][r]) * acc[1][g][c][r],
-                                  silu(acc[0][g][c + 1][r]) * acc[1][g][c + 1][r]);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + row * Ndim + col) =
-            make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      } else {
-        float* yp = static_cast<float*>(out) + row * Ndim + col;
-        *reinterpret_cast<f32x4*>(yp) =
-            f32x4{acc[0][g][0][r], acc[0][g][1][r], acc[0][g][2][r], acc[0][g][3][r]};
-        *reinterpret_cast<f32x4*>(yp + 4) =
-            f32x4{acc[0][g][4][r], acc[0][g][5][r], acc[0][g][6][r], acc[0][g][7][r]};
-      }
+      *reinterpret_cast<f32x4*>(op + col) =
+          f32x4{acc[g][0][q], acc[g][1][q], acc[g][2][q], acc[g][3][q]};
+      *reinterpret_cast<f32x4*>(op + col + 4) =
+          f32x4{acc[g][4][q], acc[g][5][q], acc[g][6][q], acc[g][7][q]};
     }
   }
 }
 
 template <bool UP, int WAVES>
-hipError_t launch_decode_t(const Shape& s, const uint16_t* act, const int32_t* cnt,
-                           const int32_t* off, const int32_t* row_slot, const uint16_t* wa,
-                           const uint16_t* wb, void* out, int Kdim, int Ndim,
-                           hipStream_t stream) {
+hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const float* ab, const int32_t* cnt,
+                           const int32_t* off, const int32_t* row_slot, const uint16_t* w0,
+                           const uint16_t* w1, void* out, int Kdim, int Ndim, int nsplit,
+                           ptrdiff_t split_stride, hipStream_t stream) {
   const int ncb = (Ndim + 127) / 128;
-  const int grid = s.n * ncb;
+  const int grid = s.n * ncb * (UP ? 2 : nsplit);
+  const int P = s.T * s.K;
+  const int klen = (Kdim + nsplit - 1) / nsplit;
   if (s.T <= kDecodeRows)
-    hipLaunchKernelGGL((decode_kernel<UP, 1, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream,
-                       act, cnt, off, row_slot, wa, wb, out, Kdim, Ndim, s.K, ncb);
-  else
-    hipLaunchKernelGGL((decode_kernel<UP, 2, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream,
-                       act, cnt, off, row_slot, wa, wb, out, Kdim, Ndim, s.K, ncb);
+    hipLaunchKernelGGL((decode_kernel<UP, 1, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream, x,
+                       ab, cnt, off, row_slot, w0, w1, out, Kdim, Ndim, s.K, P, ncb, nsplit, klen,
+                       split_stride);
+  else  // twice the accumulators: half the waves, so the registers fit without spilling
+    hipLaunchKernelGGL((decode_kernel<UP, 2, WAVES / 2>), dim3(grid), dim3(WAVES / 2 * 64), 0,
+                       stream, x, ab, cnt, off, row_slot, w0, w1, out, Kdim, Ndim, s.K, P, ncb,
+                       nsplit, klen, split_stride);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t decode_scratch_bytes(const Shape& s) {
+  return size_t(2) * s.T * s.K * s.H * 4;
+}
+
+int decode_down_splits(const Shape& s) {
+  // split the contraction when each half still gives every wave whole steps
+  return (s.H % 64 == 0 && s.H / 2 >= 32 * kDownWaves) ? 2 : 1;
+}
+
 hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
                             const int32_t* expert_offset, const int32_t* row_slot,
-                            const uint16_t* w1, const uint16_t* w3, uint16_t* h,
+                            const uint16_t* w1, const uint16_t* w3, float* ab,
                             hipStream_t stream) {
-  return launch_decode_t<true, kUpWaves>(s, x, expert_count, expert_offset, row_slot, w1, w3, h,
-                                         s.D, s.H, stream);
+  return launch_decode_t<true, kUpWaves>(s, x, nullptr, expert_count, expert_offset, row_slot,
+                                         w1, w3, ab, s.D, s.H, 1, 0, stream);
 }
 
 hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
-                              const int32_t* expert_offset, const uint16_t* h,
-                              const uint16_t* w2, float* y_rows, hipStream_t stream) {
-  return launch_decode_t<false, kDownWaves>(s, h, expert_count, expert_offset, nullptr, w2,
-                                            nullptr, y_rows, s.H, s.D, stream);
+                              const int32_t* expert_offset, const int32_t* row_slot,
+                              const float* ab, const uint16_t* w2, float* y_rows, int nsplit,
+                              ptrdiff_t split_stride, hipStream_t stream) {
+  return launch_decode_t<false, kDownWaves>(s, nullptr, ab, expert_count, expert_offset, row_slot,
+                                            w2, nullptr, y_rows, s.H, s.D, nsplit, split_stride,
+                                            stream);
 }
 
 }  // namespace moe

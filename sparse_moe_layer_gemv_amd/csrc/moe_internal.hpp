@@ -43,13 +43,20 @@ hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, con
                                hipStream_t stream);
 
 // Weight-streaming path for small T (every touched expert's weights read once).
+// The first product writes fp32 a = x w1 and b = x w3 per token-slot into
+// `ab` ([2][T*K][H], decode_scratch_bytes); the second forms h = silu(a) * b
+// on the fly and may split its contraction into `nsplit` partial sums
+// (decode_down_splits), partial ks at y_rows + ks * split_stride.
+size_t decode_scratch_bytes(const Shape& s);
+int decode_down_splits(const Shape& s);
 hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
                             const int32_t* expert_offset, const int32_t* row_slot,
-                            const uint16_t* w1, const uint16_t* w3, uint16_t* h,
+                            const uint16_t* w1, const uint16_t* w3, float* ab,
                             hipStream_t stream);
 hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
-                              const int32_t* expert_offset, const uint16_t* h,
-                              const uint16_t* w2, float* y_rows, hipStream_t stream);
+                              const int32_t* expert_offset, const int32_t* row_slot,
+                              const float* ab, const uint16_t* w2, float* y_rows, int nsplit,
+                              ptrdiff_t split_stride, hipStream_t stream);
 
 // out[t] = sum_k gate[t][k] * (sum_p y_rows[p * split_stride + row(t,k)]),
 // partials p summed first, in order.
