@@ -3,17 +3,16 @@
 // is the softmax of the Top-K logits of a linear layer; logits outside the
 // top K are set to -inf, so they get a gate of exactly zero.
 //
-// A workgroup of 4 wavefronts owns TPW consecutive tokens and splits the dim
-// axis between its waves: lane l of wave w reads the 16-byte steps
-// 8*(64*w + l) + 2048*i, so each token row is read as coalesced 1 KiB
-// segments, and every W_g row is loaded once per step and reused for the TPW
-// tokens.  The n partial sums per token are reduced across each wave with a
-// butterfly and across the 4 waves through LDS in a fixed order; then lane t
-// of wave 0 picks the top K of token t in registers (strict ">" so the lower
-// expert index wins a tie) and writes the softmax over the kept logits.
-// The kernel is bound by reading x from HBM (n = 8 multiply-adds per 2-byte
-// element); splitting the dim axis over 4 waves keeps small batches (decode)
-// from being one long dependent chain of loads.
+// A workgroup of 256 threads owns TPW consecutive tokens and splits the dim
+// axis between its threads: thread i reads the 16-byte steps 8*i + 2048*j, so
+// each token row is read as coalesced 1 KiB segments, and every W_g row is
+// loaded once per step and reused for the TPW tokens.  The TPW*NE partial sums
+// of the 256 threads are reduced through LDS in two fixed-order stages (no
+// atomics, deterministic), then thread t picks the top K of token t (strict
+// ">" so the lower expert index wins a tie) and writes the softmax over the
+// kept logits.  The kernel is bound by reading x from HBM (n = 8 multiply-adds
+// per 2-byte element) and by its latency at small batches, so it is kept
+// short: no unrolled cross-lane shuffles, one compact epilogue.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -28,10 +27,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T, int D, int n,
     int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
     float* __restrict__ logits) {
-  constexpr int kWaves = kRouterThreads / 64;
-  __shared__ float red[kWaves][TPW][NE];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int R = TPW * NE;                 // values per workgroup: (token, expert)
+  constexpr int TPR = kRouterThreads / R;     // threads per value in the first stage
+  static_assert(kRouterThreads % R == 0, "values must divide the threads");
+  __shared__ float part[kRouterThreads][R + 1];   // +1: spread the column reads over banks
+  __shared__ float stage1[R][TPR];
+  __shared__ float total[R];
+  const int tid = threadIdx.x;
   const int t0 = blockIdx.x * TPW;
 
   float acc[TPW][NE];
@@ -40,15 +42,12 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[t][e] = 0.f;
 
-  for (int k = (wave * 64 + lane) * 8; k < D; k += kRouterThreads * 8) {
+  for (int k = tid * 8; k < D; k += kRouterThreads * 8) {
     uint4 xv[TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      if (t0 + t < T)
-        xv[t] = *reinterpret_cast<const uint4*>(x + size_t(t0 + t) * D + k);
-      else
-        xv[t] = make_uint4(0, 0, 0, 0);
-    }
+    for (int t = 0; t < TPW; ++t)
+      xv[t] = (t0 + t < T) ? *reinterpret_cast<const uint4*>(x + size_t(t0 + t) * D + k)
+                           : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float w[NE];
@@ -77,74 +76,58 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     }
   }
 
+  // reduction: part[thread][value]; stage 1 sums TPR contiguous runs of
+  // threads per value, stage 2 sums the runs, both in increasing order
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const float v = wave_sum(acc[t][e]);
-      if (lane == 0) red[wave][t][e] = v;
-    }
+    for (int e = 0; e < NE; ++e) part[tid][t * NE + e] = acc[t][e];
   __syncthreads();
-  if (wave != 0) return;
-
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tok = t0 + t;
-    if (lane != t || tok >= T) continue;
-    float l[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      float v = red[0][t][e];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) v += red[w][t][e];
-      l[e] = v;
-    }
-    if (logits) {
-#pragma unroll
-      for (int e = 0; e < NE; ++e)
-        if (e < n) logits[size_t(tok) * n + e] = l[e];
-    }
-    // Top-K by repeated selection: strictly larger wins, so ties keep the
-    // lower index, and slot order is decreasing logit.
-    uint64_t taken = 0;
-    float kept[NE];
-    int kidx[NE];
-#pragma unroll
-    for (int s = 0; s < NE; ++s) {
-      kept[s] = 0.f;
-      kidx[s] = 0;
-      if (s < K) {
-        int bi = -1;
-        float bv = 0.f;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          if (e < n && !((taken >> e) & 1ull) && (bi < 0 || l[e] > bv)) {
-            bi = e;
-            bv = l[e];
-          }
-        }
-        taken |= 1ull << bi;
-        kept[s] = bv;
-        kidx[s] = bi;
-      }
-    }
-    // Softmax over the kept logits (exp(-inf) = 0 for the rest), shifted by
-    // the largest, which is slot 0.
-    float ex[NE];
+  {
+    const int v = tid / TPR, c = tid - v * TPR;
+    constexpr int RUN = kRouterThreads / TPR;
     float sum = 0.f;
-#pragma unroll
-    for (int s = 0; s < NE; ++s) {
-      ex[s] = (s < K) ? __expf(kept[s] - kept[0]) : 0.f;
-      sum += ex[s];
-    }
-#pragma unroll
-    for (int s = 0; s < NE; ++s) {
-      if (s < K) {
-        topk_idx[size_t(tok) * K + s] = kidx[s];
-        topk_gate[size_t(tok) * K + s] = ex[s] / sum;
-      }
-    }
+    for (int i = 0; i < RUN; ++i) sum += part[c * RUN + i][v];
+    stage1[v][c] = sum;
   }
+  __syncthreads();
+  if (tid < R) {
+    float sum = 0.f;
+    for (int c = 0; c < TPR; ++c) sum += stage1[tid][c];
+    total[tid] = sum;
+  }
+  __syncthreads();
+  if (tid >= TPW || t0 + tid >= T) return;
+
+  const int tok = t0 + tid;
+  float l[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) l[e] = total[tid * NE + e];
+  if (logits)
+    for (int e = 0; e < n; ++e) logits[size_t(tok) * n + e] = l[e];
+  // Top-K by repeated selection: strictly larger wins, so ties keep the lower
+  // index, and slot order is decreasing logit.  Softmax over the kept logits
+  // (exp(-inf) = 0 for the rest), shifted by the largest, which is slot 0.
+  uint64_t taken = 0;
+  float top = 0.f, sum = 0.f;
+  for (int s = 0; s < K; ++s) {
+    int bi = -1;
+    float bv = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      if (e < n && !((taken >> e) & 1ull) && (bi < 0 || l[e] > bv)) {
+        bi = e;
+        bv = l[e];
+      }
+    taken |= 1ull << bi;
+    if (s == 0) top = bv;
+    const float ex = __expf(bv - top);
+    sum += ex;
+    topk_idx[size_t(tok) * K + s] = bi;
+    topk_gate[size_t(tok) * K + s] = ex;
+  }
+  const float inv = 1.f / sum;
+  for (int s = 0; s < K; ++s) topk_gate[size_t(tok) * K + s] *= inv;
 }
 
 template <int NE, int TPW, bool VEC>
