@@ -207,6 +207,8 @@ def main(argv=None):
             e6 = evs[s][c]
             for i, k in enumerate(STAGES):
                 stage_ms[k].append(ev.elapsed_ms(e6[i], e6[i + 1]))
+    # per-step layer time on the GPU (first stage start to last stage end)
+    step_gpu_ms = [ev.elapsed_ms(evs[s][0][0], evs[s][n_chunks - 1][len(STAGES)]) for s in range(args.steps)]
     ev.close()
     # per-launch averages (one launch of each stage per chunk)
     stage_avg = {k: float(np.mean(v)) for k, v in stage_ms.items()}
@@ -256,6 +258,8 @@ def main(argv=None):
         "tflops": tflops,
         "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
         "stage_ms": stage_avg,
+        "step_gpu_ms": {"median": float(np.median(step_gpu_ms)), "min": float(np.min(step_gpu_ms)),
+                        "mean": float(np.mean(step_gpu_ms))},
         "expert_counts": counts.tolist(),
         "roofline": roof,
     }
