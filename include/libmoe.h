@@ -169,6 +169,20 @@ moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void
                                int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
                                void* stream, void* const* events);
 
+/* Routing diagnostics ("Mixtral of Experts", section 5, Routing analysis:
+ * the per-expert token shares of Figure 7 and Figure 9, the consecutive-token
+ * repetition rates of Table 5), as exact integer counts.
+ *   topk_idx  int32 [T][K]  in: slot 0 is the first choice
+ *   counts    int32 [2n+2]  out (device): [0, n) slots per expert among first
+ *             choices; [n, 2n) slots per expert over all K choices; [2n] tokens
+ *             t < T-1 whose first choice equals token t+1's; [2n+1] tokens
+ *             t < T-1 that share any chosen expert with token t+1.
+ * Ids outside [0, n) are not counted and match nothing.  Unlike the other
+ * calls, T = 0 still writes the (zero) counts.  Shares and rates are these
+ * counts divided by T, T*K or T-1 on the host. */
+moe_status_t moe_route_stats(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                             void* stream);
+
 /* Largest T for which moe_forward and moe_grouped_ffn take the weight-streaming
  * (decode) path. */
 int32_t moe_decode_max_tokens(void);

@@ -223,6 +223,37 @@ def consecutive_repeat(idx: np.ndarray):
     return float(first), float(either)
 
 
+def route_stats(idx: np.ndarray, n: int) -> dict:
+    """Exact routing counts over a [T][K] choice array ("Mixtral of Experts",
+    section 5: the per-expert shares of Figure 7 / Figure 9 as first choice and
+    as either choice, and the consecutive-token repetitions of Table 5).
+
+    Ids outside [0, n) are not counted and match nothing.  Returns plain ints:
+    first[e], any[e] (slot counts), repeat_first (tokens t < T-1 whose first
+    choice equals token t+1's) and repeat_either (tokens t < T-1 sharing any
+    chosen expert with token t+1)."""
+    idx = np.asarray(idx)
+    T = idx.shape[0]
+    first = [0] * n
+    anyc = [0] * n
+    rep_first = rep_either = 0
+    for t in range(T):
+        row = [int(v) for v in idx[t]]
+        if 0 <= row[0] < n:
+            first[row[0]] += 1
+        for v in row:
+            if 0 <= v < n:
+                anyc[v] += 1
+        if t + 1 < T:
+            nxt = [int(v) for v in idx[t + 1]]
+            valid = [v for v in row if 0 <= v < n]
+            if 0 <= row[0] < n and nxt[0] == row[0]:
+                rep_first += 1
+            if any(v in nxt for v in valid):
+                rep_either += 1
+    return {"first": first, "any": anyc, "repeat_first": rep_first, "repeat_either": rep_either}
+
+
 # ---------------------------------------------------------------------------
 # parity comparison helper used by the tests
 # ---------------------------------------------------------------------------

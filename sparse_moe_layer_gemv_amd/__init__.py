@@ -29,7 +29,7 @@ MAX_EXPERTS = 64
 
 EXPORTED = ("moe_capacity_rows", "moe_workspace_bytes", "moe_status_string", "moe_route",
             "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-            "moe_decode_max_tokens", "moe_forward_timed")
+            "moe_decode_max_tokens", "moe_forward_timed", "moe_route_stats")
 
 
 for _name in EXPORTED:
@@ -57,11 +57,12 @@ lib.moe_route.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.moe_permute.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.moe_grouped_ffn.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.moe_combine.argtypes = [_P, _vp, _vp, _vp, _vp, _vp]
+lib.moe_route_stats.argtypes = [_P, _vp, _vp, _vp]
 lib.moe_forward.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.moe_forward_timed.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   _vp, ctypes.POINTER(_vp)]
 for _f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-           "moe_forward_timed"):
+           "moe_forward_timed", "moe_route_stats"):
     getattr(lib, _f).restype = ctypes.c_int32
 
 
@@ -216,6 +217,27 @@ def combine(y_rows, slot_row, topk_gate, out_dtype: int = MOE_F32, out=None, str
         _ptr(out, (torch.float32,) if out_dtype == MOE_F32 else _bf16(), (T, D), "out"),
         _stream(stream)))
     return out
+
+
+def route_stats(topk_idx, n_experts: int, counts=None, stream=None):
+    """moe_route_stats: routing diagnostics of a [T][K] expert choice tensor.
+
+    Returns a dict of host ints / lists: ``first`` (slots per expert among
+    first choices), ``any`` (slots per expert over all choices),
+    ``repeat_first`` and ``repeat_either`` (consecutive-token counts), and
+    ``counts`` (the raw int32 device tensor [2n+2])."""
+    torch = _torch()
+    T, K = topk_idx.shape
+    n = int(n_experts)
+    p = problem(T, 8, 8, n, K)
+    if counts is None:
+        counts = torch.empty(2 * n + 2, dtype=torch.int32, device=topk_idx.device)
+    _check("moe_route_stats", lib.moe_route_stats(
+        ctypes.byref(p), _ptr(topk_idx, torch.int32, (T, K), "topk_idx") if T else None,
+        _ptr(counts, torch.int32, (2 * n + 2,), "counts"), _stream(stream)))
+    c = counts.cpu().tolist()
+    return {"first": c[:n], "any": c[n:2 * n], "repeat_first": c[2 * n],
+            "repeat_either": c[2 * n + 1], "counts": counts}
 
 
 def forward(x, w_gate, w1, w3, w2, top_k: int, out=None, topk_idx=None, topk_gate=None,

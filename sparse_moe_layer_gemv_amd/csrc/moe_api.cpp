@@ -218,6 +218,18 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int3
                                         static_cast<hipStream_t>(stream)));
 }
 
+static_assert(moe::kMaxStatExperts >= MOE_MAX_EXPERTS, "histogram covers every expert");
+
+moe_status_t moe_route_stats(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                             void* stream) {
+  Shape s;
+  moe_status_t st = check_problem(p, &s);
+  if (st != MOE_OK) return st;
+  if (!counts || (s.T > 0 && !topk_idx)) return MOE_EINVAL;
+  if (!aligned16(counts) || (topk_idx && !aligned16(topk_idx))) return MOE_EINVAL;
+  return hip_status(moe::launch_route_stats(s, topk_idx, counts, static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_gate,
                          const void* w1, const void* w3, const void* w2, void* out,
                          int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,

@@ -64,6 +64,11 @@ hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_
                           const int32_t* slot_row, const float* topk_gate, void* out,
                           bool out_bf16, hipStream_t stream);
 
+// Routing diagnostics: counts [2n + 2] (see moe_route_stats).
+constexpr int kMaxStatExperts = 64;
+hipError_t launch_route_stats(const Shape& s, const int32_t* topk_idx, int32_t* counts,
+                              hipStream_t stream);
+
 // y_rows[r] += y_part[r] for the rows of the expert segments (r < offset[n]).
 hipError_t launch_add_rows(const Shape& s, const int32_t* expert_offset, float* y_rows,
                            const float* y_part, hipStream_t stream);

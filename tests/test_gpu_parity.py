@@ -60,6 +60,10 @@ SHAPES = [
     ("n16_k4", 130, 256, 384, 16, 4, 20),
     ("n6_k3", 90, 136, 200, 6, 3, 21),
     ("n64_k2", 400, 128, 256, 64, 2, 22),
+    # K = n: every expert on every token, the dense softmax mixture
+    ("dense_k8", 300, 256, 384, 8, 8, 23),
+    ("decode_dense_k8", 8, 256, 384, 8, 8, 24),
+    ("k4_n32", 520, 256, 512, 32, 4, 25),
 ]
 
 

@@ -259,3 +259,35 @@ def test_repetition_rate_detects_structure():
     first, either = moe_ref.consecutive_repeat(idx)
     assert first == 0.25
     assert either == 0.75
+
+
+def test_route_stats_counts_agree_with_the_rates_and_a_hand_example(golden):
+    # the hand example above, as exact counts
+    idx = np.array([[0, 1], [0, 2], [2, 3], [4, 5], [5, 4]])
+    st = moe_ref.route_stats(idx, 8)
+    assert st["first"] == [2, 0, 1, 0, 1, 1, 0, 0]
+    assert st["any"] == [2, 1, 2, 1, 2, 2, 0, 0]
+    assert (st["repeat_first"], st["repeat_either"]) == (1, 3)
+    # random assignment: counts / denominators are the section-5 rates
+    cf = golden["routing_closed_forms"]
+    rng = np.random.default_rng(15)
+    idx = moe_ref.topk_indices(rng.standard_normal((20000, 8)), 2)
+    st = moe_ref.route_stats(idx, 8)
+    first, either = moe_ref.consecutive_repeat(idx)
+    assert st["repeat_first"] == round(first * (len(idx) - 1))
+    assert st["repeat_either"] == round(either * (len(idx) - 1))
+    assert np.array_equal(np.array(st["any"]) / idx.size, moe_ref.expert_share(idx, 8))
+    assert sum(st["first"]) == len(idx) and sum(st["any"]) == idx.size
+    assert abs(st["repeat_either"] / (len(idx) - 1) - cf["either_choice_repeat"]) < 0.02
+
+
+def test_route_stats_ignores_out_of_range_ids():
+    # -1 and 8 are dropped slots: never counted, never matched (not even by
+    # another dropped slot)
+    idx = np.array([[-1, 3], [-1, 3], [8, 2], [8, 5], [1, -1]])
+    st = moe_ref.route_stats(idx, 8)
+    assert st["first"] == [0, 1, 0, 0, 0, 0, 0, 0]
+    assert st["any"] == [0, 1, 1, 2, 0, 1, 0, 0]
+    # t=0->1 share 3 (first choices both dropped: no first repeat); 1->2 none;
+    # 2->3 none (8 matches nothing); 3->4 none
+    assert (st["repeat_first"], st["repeat_either"]) == (0, 1)
