@@ -142,6 +142,59 @@ def cpu_baseline(name, inputs, sample_tokens, min_seconds=10.0):
                       f"fp64 numpy oracle run {reps}x, {dt:.1f} s wall", "cpu": cpu}
 
 
+def crossover(args, torch, moe):
+    """Small-batch sweep ("Mixtral of Experts", section 3, remark on small
+    batches; the summary's limitations): at each T the layer runs once with the
+    weight-streaming expert path (while T <= decode_max_tokens) and once with
+    the tiled matrix-core path, same inputs and weights (the Mixtral-shape
+    decode weight set).  Reports per-step GPU time, the weight bytes of the
+    touched experts per second, TFLOP/s, and the largest T at which streaming
+    is faster."""
+    w = moe_synth.WORKLOADS["decode"]
+    D, H, n, K = w.D, w.H, w.n, w.K
+    log("[crossover] generating Mixtral-shape weights")
+    L = moe_synth.make_workload("decode")
+    wg, w1, w3, w2 = (to_dev(a) for a in (L.w_gate, L.w1, L.w3, L.w2))
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+    rows = []
+    for T in (1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 192, 256):
+        x = to_dev(moe_synth.make_x(w.x_seed, T, D))
+        idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
+        out = torch.empty((T, D), dtype=torch.float32, device="cuda:0")
+        row = {"T": T}
+        for name, path in (("stream", moe.PATH_STREAM), ("tiled", moe.PATH_TILED)):
+            nbytes = moe.workspace_bytes(moe.problem(T, D, H, n, K, path=path))
+            if nbytes == 0:  # streaming beyond the batch sizes it supports
+                continue
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+            run = lambda e=None: moe.forward(x, wg, w1, w3, w2, K, out=out, topk_idx=idx,
+                                             workspace=ws, stream=stream, events=e, path=path)
+            for _ in range(args.warmup):
+                run()
+            evs = [ev.create(6) for _ in range(args.steps)]
+            for e6 in evs:
+                run(e6)
+            torch.cuda.synchronize()
+            ms = float(np.median([ev.elapsed_ms(e6[0], e6[5]) for e6 in evs]))
+            touched = int((np.bincount(idx.cpu().numpy().ravel(), minlength=n) > 0).sum())
+            wbytes = touched * 3 * D * H * 2
+            row[name] = {"ms": ms, "weight_gbs": wbytes / (ms / 1e3) / 1e9,
+                         "tflops": layer_flops(T, D, H, n, K) / (ms / 1e3) / 1e12}
+            log(f"[crossover] T={T} {name}: {ms * 1e3:.1f} us")
+        rows.append(row)
+    ev.close()
+    faster = [r["T"] for r in rows if "stream" in r and r["stream"]["ms"] < r["tiled"]["ms"]]
+    rec = {"metric": "small-batch crossover: layer time by expert-product path",
+           "unit": "ms", "data": "synthetic", "dtype": "bf16",
+           "config": {"workload": "decode weights, T swept", "dim": D, "hidden": H, "n_experts": n,
+                      "top_k": K, "steps": args.steps, "warmup": args.warmup},
+           "rows": rows, "stream_faster_up_to_T": max(faster) if faster else 0,
+           "library_threshold_T": moe.decode_max_tokens()}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +204,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens for the oracle timing (default: a bounded sample per workload)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="small-batch sweep: time both expert-product paths for T = 1..256 and "
+                         "print one JSON line with the measured crossover")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -162,6 +218,9 @@ def main(argv=None):
     import torch
     import sparse_moe_layer_gemv_amd as moe
     from sparse_moe_layer_gemv_amd.profiling import load_traffic
+
+    if args.crossover:
+        return crossover(args, torch, moe)
 
     w = moe_synth.WORKLOADS[args.workload]
     T, D, H, n, K = w.T, w.D, w.H, w.n, w.K

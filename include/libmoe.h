@@ -66,6 +66,13 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
+/* Expert-product path.  AUTO takes the weight-streaming kernels for
+ * T <= moe_decode_max_tokens() and the tiled matrix-core kernels above.
+ * STREAM forces the weight-streaming path (T <= 64, MOE_ENOTSUP above); TILED
+ * forces the tiled path at any T.  Both give results within the same
+ * tolerance of the exact layer; they are not bit-identical to each other. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_path_t;
+
 typedef struct {
   int32_t tokens;     /* T >= 0 */
   int32_t dim;        /* D, multiple of 8 */
@@ -73,6 +80,7 @@ typedef struct {
   int32_t n_experts;  /* n, 1..64 */
   int32_t top_k;      /* K, 1..n */
   int32_t out_dtype;  /* moe_dtype_t of the layer output `out` */
+  int32_t path;       /* moe_path_t: which expert-product kernels to use */
 } moe_problem_t;
 
 /* Number of rows of the permuted layout: T*K + n*(MOE_TILE_M-1) rounded up to

@@ -24,6 +24,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
+PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
 TILE_M = 256
 MAX_EXPERTS = 64
 
@@ -40,7 +41,7 @@ for _name in EXPORTED:
 class Problem(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int32), ("dim", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(Problem)
@@ -78,8 +79,8 @@ def _check(fn: str, status: int):
 
 
 def problem(tokens: int, dim: int, hidden: int, n_experts: int, top_k: int,
-            out_dtype: int = MOE_F32) -> Problem:
-    return Problem(tokens, dim, hidden, n_experts, top_k, out_dtype)
+            out_dtype: int = MOE_F32, path: int = 0) -> Problem:
+    return Problem(tokens, dim, hidden, n_experts, top_k, out_dtype, path)
 
 
 def capacity_rows(p: Problem) -> int:
@@ -132,12 +133,12 @@ def _bf16():
     return (torch.bfloat16, torch.uint16, torch.int16)
 
 
-def _shape_of(x, w1, top_k, out_dtype=MOE_F32) -> Problem:
+def _shape_of(x, w1, top_k, out_dtype=MOE_F32, path=PATH_AUTO) -> Problem:
     T, D = x.shape
     n, D2, H = w1.shape
     if D2 != D:
         raise ValueError(f"w1 has dim {D2}, x has dim {D}")
-    return problem(T, D, H, n, top_k, out_dtype)
+    return problem(T, D, H, n, top_k, out_dtype, path)
 
 
 def route(x, w_gate, top_k: int, topk_idx=None, topk_gate=None, logits=None, stream=None):
@@ -180,10 +181,10 @@ def permute(topk_idx, n_experts: int, stream=None, out=None):
 
 
 def grouped_ffn(x, expert_count, expert_offset, row_slot, w1, w3, w2, top_k: int,
-                y_rows=None, workspace=None, stream=None):
+                y_rows=None, workspace=None, stream=None, path: int = PATH_AUTO):
     """moe_grouped_ffn: returns y_rows fp32 [cap][D]."""
     torch = _torch()
-    p = _shape_of(x, w1, top_k)
+    p = _shape_of(x, w1, top_k, MOE_F32, path)
     T, D, H, n = p.tokens, p.dim, p.hidden, p.n_experts
     cap = capacity_rows(p)
     if y_rows is None:
@@ -241,13 +242,15 @@ def route_stats(topk_idx, n_experts: int, counts=None, stream=None):
 
 
 def forward(x, w_gate, w1, w3, w2, top_k: int, out=None, topk_idx=None, topk_gate=None,
-            workspace=None, out_dtype: int = MOE_F32, stream=None, events=None):
+            workspace=None, out_dtype: int = MOE_F32, stream=None, events=None,
+            path: int = PATH_AUTO):
     """moe_forward: the whole layer.  Returns out [T][D].
 
     ``events``: optional sequence of 6 raw hipEvent_t handles; then
-    moe_forward_timed records them between the stages."""
+    moe_forward_timed records them between the stages.  ``path``: PATH_AUTO,
+    PATH_STREAM (weight streaming, T <= decode_max_tokens()) or PATH_TILED."""
     torch = _torch()
-    p = _shape_of(x, w1, top_k, out_dtype)
+    p = _shape_of(x, w1, top_k, out_dtype, path)
     T, D, H, n = p.tokens, p.dim, p.hidden, p.n_experts
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16 if out_dtype == MOE_BF16 else torch.float32,

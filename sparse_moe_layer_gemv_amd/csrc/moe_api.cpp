@@ -28,6 +28,9 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
   if (p->top_k > p->n_experts) return MOE_EINVAL;
   if (p->dim % 8 != 0 || p->hidden % 8 != 0) return MOE_EINVAL;
   if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return MOE_EINVAL;
+  if (p->path != MOE_PATH_AUTO && p->path != MOE_PATH_STREAM && p->path != MOE_PATH_TILED)
+    return MOE_EINVAL;
+  if (p->path == MOE_PATH_STREAM && p->tokens > moe::kStreamMaxTokens) return MOE_ENOTSUP;
   if (p->n_experts > MOE_MAX_EXPERTS) return MOE_ENOTSUP;
   const int64_t P = int64_t(p->tokens) * p->top_k;
   const int64_t cap =
@@ -44,6 +47,8 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
   s->n = p->n_experts;
   s->K = p->top_k;
   s->cap = cap;
+  s->stream = p->path == MOE_PATH_STREAM ||
+              (p->path == MOE_PATH_AUTO && p->tokens <= moe::kDecodeMaxTokens);
   return MOE_OK;
 }
 
@@ -71,7 +76,7 @@ Carve carve(const Shape& s) {
   c.row_slot = o; o = align_up(o + size_t(s.cap) * 4, kAlign);
   c.slot_row = o; o = align_up(o + P * 4, kAlign);
   size_t h_bytes = size_t(s.cap) * s.H * 2;
-  if (s.T <= moe::kDecodeMaxTokens) h_bytes = std::max(h_bytes, moe::decode_scratch_bytes(s));
+  if (s.stream) h_bytes = std::max(h_bytes, moe::decode_scratch_bytes(s));
   c.h = o;        o = align_up(o + h_bytes, kAlign);
   c.y = o;        o = align_up(o + size_t(kMaxSplits) * s.cap * s.D * 4, kAlign);
   c.total = o;
@@ -80,7 +85,7 @@ Carve carve(const Shape& s) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-bool use_decode(const Shape& s) { return s.T <= moe::kDecodeMaxTokens; }
+bool use_decode(const Shape& s) { return s.stream; }
 
 // `mark(i)`, when given, records stage event i (3 after the first product, 4
 // after the second).

@@ -3,7 +3,7 @@
 // The pages note that a sparse MoE layer pays extra memory loads and loses
 // efficiency at small batch sizes ("Mixtral of Experts", section 3, remark on
 // hardware utilisation; the aipaper.jasonlin.tech summary, limitations).  With
-// T <= 32 tokens each expert sees only a handful of rows, so the expert
+// T <= 64 tokens each expert sees only a handful of rows, so the expert
 // products are bound by reading the weights: every touched expert's w1, w3
 // and w2 must cross HBM once and nothing else matters.  These kernels do
 // exactly that read, once, coalesced, with many loads in flight, and use the
@@ -213,12 +213,19 @@ hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const float* ab, c
   const int grid = s.n * ncb * (UP ? 2 : nsplit);
   const int P = s.T * s.K;
   const int klen = (Kdim + nsplit - 1) / nsplit;
+  // more token rows per lane means more accumulators: fewer waves, so the
+  // registers fit without spilling
+  static_assert(kStreamMaxTokens <= 4 * kDecodeRows, "four row groups per lane at most");
   if (s.T <= kDecodeRows)
     hipLaunchKernelGGL((decode_kernel<UP, 1, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream, x,
                        ab, cnt, off, row_slot, w0, w1, out, Kdim, Ndim, s.K, P, ncb, nsplit, klen,
                        split_stride);
-  else  // twice the accumulators: half the waves, so the registers fit without spilling
+  else if (s.T <= 2 * kDecodeRows)
     hipLaunchKernelGGL((decode_kernel<UP, 2, WAVES / 2>), dim3(grid), dim3(WAVES / 2 * 64), 0,
+                       stream, x, ab, cnt, off, row_slot, w0, w1, out, Kdim, Ndim, s.K, P, ncb,
+                       nsplit, klen, split_stride);
+  else
+    hipLaunchKernelGGL((decode_kernel<UP, 4, WAVES / 2>), dim3(grid), dim3(WAVES / 2 * 64), 0,
                        stream, x, ab, cnt, off, row_slot, w0, w1, out, Kdim, Ndim, s.K, P, ncb,
                        nsplit, klen, split_stride);
   return hipGetLastError();

@@ -11,14 +11,20 @@ namespace moe {
 
 // Permuted-layout granule (rows per expert segment step); equals MOE_TILE_M.
 constexpr int kTileM = 256;
-// Largest T served by the weight-streaming (decode) expert path.
-constexpr int kDecodeMaxTokens = 32;
+// Largest T the weight-streaming (decode) expert path supports: every expert
+// then holds at most 64 token rows (4 groups of 16 per lane).
+constexpr int kStreamMaxTokens = 64;
+// Largest T for which the automatic path choice streams: the small-batch sweep
+// (Mixtral shape) measures streaming faster up to T = 48 and the tiled path
+// faster from T = 64 on.
+constexpr int kDecodeMaxTokens = 48;
 // Token rows handled together by one decode pass (one 16x16 MFMA column block).
 constexpr int kDecodeRows = 16;
 
 struct Shape {
   int T, D, H, n, K;
   int64_t cap;  // rows of the permuted layout
+  bool stream;  // expert products by weight streaming (else tiled)
 };
 
 hipError_t launch_route(const Shape& s, const uint16_t* x, const uint16_t* w_gate,

@@ -59,6 +59,15 @@ def test_capacity_and_workspace(moe):
     assert moe.workspace_bytes(moe.problem(16, 4100, 14336, 8, 2)) == 0    # dim % 8
     assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 65, 2)) == 0   # n > 64
     assert moe.decode_max_tokens() >= 16
+    # expert-product path: unknown values are invalid; forced streaming only up
+    # to decode_max_tokens(); its scratch is part of the workspace
+    assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 8, 2, path=3)) == 0
+    assert moe.workspace_bytes(moe.problem(64, 4096, 14336, 8, 2, path=moe.PATH_STREAM)) > 0
+    big = 65
+    assert moe.workspace_bytes(moe.problem(big, 4096, 14336, 8, 2, path=moe.PATH_STREAM)) == 0
+    assert moe.workspace_bytes(moe.problem(big, 4096, 14336, 8, 2, path=moe.PATH_TILED)) > 0
+    assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 8, 2, path=moe.PATH_STREAM)) >= \
+        2 * 16 * 2 * 14336 * 4
 
 
 def test_status_strings(moe):

@@ -1,7 +1,7 @@
 """GPU parity of every libmoe entry point against the fp64 oracle, at sizes the
 oracle finishes in seconds: several row/column/contraction tiles, ragged
-tails, both expert paths (weight streaming for T <= 32, matrix-core tiles
-above), forced skewed and empty-expert routings, K and n variants."""
+tails, both expert paths (weight streaming for T <= 48 by default, up to 64
+when forced; matrix-core tiles above), forced skewed and empty-expert routings, K and n variants."""
 import numpy as np
 import pytest
 
@@ -55,7 +55,9 @@ SHAPES = [
     ("decode_t16", 16, 512, 1024, 8, 2, 15),
     ("decode_t17", 17, 512, 1024, 8, 2, 16),
     ("decode_t32", 32, 384, 640, 8, 2, 17),
-    ("mfma_t33", 33, 512, 1024, 8, 2, 18),
+    ("stream_t33", 33, 512, 1024, 8, 2, 18),
+    ("stream_t48", 48, 512, 1024, 8, 2, 26),
+    ("tiled_t49", 49, 512, 1024, 8, 2, 27),
     ("k1_switch", 200, 256, 512, 8, 1, 19),
     ("n16_k4", 130, 256, 384, 16, 4, 20),
     ("n6_k3", 90, 136, 200, 6, 3, 21),
@@ -188,3 +190,32 @@ def test_zero_tokens_is_a_noop(moe):
     moe.forward(d["x"][:0], d["wg"], d["w1"], d["w3"], d["w2"], 2, out=out,
                 workspace=torch.empty(256, dtype=torch.uint8, device="cuda:0"))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,path", [(16, 2), (1, 2), (32, 2), (24, 1), (5, 1), (64, 1), (60, 1)],
+                         ids=["tiled_t16", "tiled_t1", "tiled_t32", "stream_t24", "stream_t5",
+                              "stream_t64", "stream_t60"])
+def test_forced_expert_path(moe, T, path):
+    # both expert-product paths at batch sizes where the other one is the default
+    L = moe_synth.make_layer(T, 512, 1024, 8, 2, seed=90 + T)
+    d = _upload(L)
+    out = moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, path=path)
+    logits = moe_ref.router_logits(L.x, L.w_gate)
+    import torch
+    idx = torch.empty((T, 2), dtype=torch.int32, device="cuda:0")
+    gate = torch.empty((T, 2), dtype=torch.float32, device="cuda:0")
+    moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, topk_idx=idx, topk_gate=gate, path=path)
+    rr = parity.check_routing(logits, 2, host(idx), host(gate))
+    assert rr.ok, rr
+    ref = moe_ref.moe_layer(L.x, L.w_gate, L.w1, L.w3, L.w2, 2, forced_idx=rr.forced_idx)
+    orep = parity.check_output(ref["y"], host(out))
+    assert orep.ok, orep
+
+
+def test_stream_path_rejects_large_batches(moe):
+    L = moe_synth.make_layer(65, 128, 256, 8, 2, seed=99)
+    d = _upload(L)
+    with pytest.raises(moe.MoeError):
+        moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, path=moe.PATH_STREAM,
+                    workspace=__import__("torch").empty(1 << 20, dtype=__import__("torch").uint8,
+                                                        device="cuda:0"))
