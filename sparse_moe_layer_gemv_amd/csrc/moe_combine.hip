@@ -11,36 +11,103 @@ namespace moe {
 namespace {
 
 constexpr int kCombineThreads = 256;
+constexpr int kCols = kCombineThreads * 4;  // columns per workgroup
 
 template <bool OUT_BF16>
+__device__ __forceinline__ void store_out(void* out, size_t at, const f32x4& acc) {
+  if constexpr (OUT_BF16) {
+    uint2 pk;
+    pk.x = pack_bf16x2(acc[0], acc[1]);
+    pk.y = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + at) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + at) = acc;
+  }
+}
+
+// One workgroup per (token, 1024-column block); each thread owns 4 columns.
+// The token's slots and gates are read once and all K (x nsplit partial) row
+// fragments are loaded before they are summed, so a small batch is one round
+// of loads deep.  KMAX bounds K for this register copy of the slots.
+template <bool OUT_BF16, int KMAX>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ y_rows, int nsplit, size_t split_stride,
-    const int32_t* __restrict__ slot_row, const float* __restrict__ gate, int D, int K,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ gate, int D, int K, int ncb,
     void* __restrict__ out) {
-  const int t = blockIdx.x;
-  for (int d = threadIdx.x * 4; d < D; d += kCombineThreads * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const int r = slot_row[size_t(t) * K + k];
-      if (r < 0) continue;
-      const float g = gate[size_t(t) * K + k];
-      f32x4 v = *reinterpret_cast<const f32x4*>(y_rows + size_t(r) * D + d);
+  const int t = blockIdx.x / ncb;
+  const int d = (blockIdx.x - t * ncb) * kCols + threadIdx.x * 4;
+  if (d >= D) return;
+  int r[KMAX];
+  float g[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    r[k] = k < K ? slot_row[size_t(t) * K + k] : -1;
+    g[k] = k < K ? gate[size_t(t) * K + k] : 0.f;
+  }
+  f32x4 v[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (r[k] >= 0) {
+      v[k] = *reinterpret_cast<const f32x4*>(y_rows + size_t(r[k]) * D + d);
       for (int p = 1; p < nsplit; ++p)
-        v += *reinterpret_cast<const f32x4*>(y_rows + p * split_stride + size_t(r) * D + d);
-      acc[0] = fmaf(g, v[0], acc[0]);
-      acc[1] = fmaf(g, v[1], acc[1]);
-      acc[2] = fmaf(g, v[2], acc[2]);
-      acc[3] = fmaf(g, v[3], acc[3]);
-    }
-    if constexpr (OUT_BF16) {
-      uint2 pk;
-      pk.x = pack_bf16x2(acc[0], acc[1]);
-      pk.y = pack_bf16x2(acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + size_t(t) * D + d) = pk;
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + size_t(t) * D + d) = acc;
+        v[k] += *reinterpret_cast<const f32x4*>(y_rows + p * split_stride + size_t(r[k]) * D + d);
     }
   }
+  // slot order; the partials of one slot were added first
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (r[k] < 0) continue;
+    acc[0] = fmaf(g[k], v[k][0], acc[0]);
+    acc[1] = fmaf(g[k], v[k][1], acc[1]);
+    acc[2] = fmaf(g[k], v[k][2], acc[2]);
+    acc[3] = fmaf(g[k], v[k][3], acc[3]);
+  }
+  store_out<OUT_BF16>(out, size_t(t) * D + d, acc);
+}
+
+// K beyond the register copy: the slots are walked in order from memory.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel_any_k(
+    const float* __restrict__ y_rows, int nsplit, size_t split_stride,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ gate, int D, int K, int ncb,
+    void* __restrict__ out) {
+  const int t = blockIdx.x / ncb;
+  const int d = (blockIdx.x - t * ncb) * kCols + threadIdx.x * 4;
+  if (d >= D) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K; ++k) {
+    const int r = slot_row[size_t(t) * K + k];
+    if (r < 0) continue;
+    const float g = gate[size_t(t) * K + k];
+    f32x4 v = *reinterpret_cast<const f32x4*>(y_rows + size_t(r) * D + d);
+    for (int p = 1; p < nsplit; ++p)
+      v += *reinterpret_cast<const f32x4*>(y_rows + p * split_stride + size_t(r) * D + d);
+    acc[0] = fmaf(g, v[0], acc[0]);
+    acc[1] = fmaf(g, v[1], acc[1]);
+    acc[2] = fmaf(g, v[2], acc[2]);
+    acc[3] = fmaf(g, v[3], acc[3]);
+  }
+  store_out<OUT_BF16>(out, size_t(t) * D + d, acc);
+}
+
+template <bool OUT_BF16>
+hipError_t launch_combine_t(const Shape& s, const float* y_rows, int nsplit, size_t split_stride,
+                            const int32_t* slot_row, const float* topk_gate, void* out,
+                            hipStream_t stream) {
+  const int ncb = (s.D + kCols - 1) / kCols;
+  const dim3 grid(unsigned(s.T) * unsigned(ncb));
+  if (s.K <= 2)
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 2>), grid, dim3(kCombineThreads), 0, stream,
+                       y_rows, nsplit, split_stride, slot_row, topk_gate, s.D, s.K, ncb, out);
+  else if (s.K <= 8)
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 8>), grid, dim3(kCombineThreads), 0, stream,
+                       y_rows, nsplit, split_stride, slot_row, topk_gate, s.D, s.K, ncb, out);
+  else
+    hipLaunchKernelGGL((combine_kernel_any_k<OUT_BF16>), grid, dim3(kCombineThreads), 0, stream,
+                       y_rows, nsplit, split_stride, slot_row, topk_gate, s.D, s.K, ncb, out);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -49,17 +116,12 @@ hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_
                           const int32_t* slot_row, const float* topk_gate, void* out,
                           bool out_bf16, hipStream_t stream) {
   if (s.T == 0) return hipSuccess;
-  if (out_bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(s.T), dim3(kCombineThreads), 0, stream, y_rows,
-                       nsplit, split_stride, slot_row, topk_gate, s.D, s.K, out);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(s.T), dim3(kCombineThreads), 0, stream, y_rows,
-                       nsplit, split_stride, slot_row, topk_gate, s.D, s.K, out);
-  return hipGetLastError();
+  return out_bf16 ? launch_combine_t<true>(s, y_rows, nsplit, split_stride, slot_row, topk_gate,
+                                           out, stream)
+                  : launch_combine_t<false>(s, y_rows, nsplit, split_stride, slot_row, topk_gate,
+                                            out, stream);
 }
 
-// Sum of the split partial products for callers of the stage API that want
-// whole rows: y_rows[r] += y_part[r] over the rows of the expert segments.
 __global__ __launch_bounds__(kCombineThreads) void add_rows_kernel(
     const int32_t* __restrict__ expert_offset, int n, int D, float* __restrict__ y,
     const float* __restrict__ y_part) {
