@@ -14,6 +14,8 @@
  *            with a non-zero gate (skipping zero gates is exact)
  *
  * Mixtral uses n = 8 experts and K = 2 (Table 1: dim 4096, hidden_dim 14336).
+ * The same calls serve the "fine-grained" layout the ai360xpert.com summary
+ * mentions (many much smaller experts, e.g. 8 of 160): n up to 256.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -34,7 +36,7 @@
  *    kernel launch returns MOE_EHIP.  tokens == 0 is a valid no-op.  No C++
  *    exception crosses this interface.
  *  - Pointers must be 16-byte aligned; dim and hidden must be multiples of 8;
- *    1 <= top_k <= n_experts <= 64.
+ *    1 <= top_k <= n_experts <= MOE_MAX_EXPERTS.
  *  - Ties in TopK go to the lower expert index; slot 0 of each token holds the
  *    larger logit.  Gates are fp32.
  *  - Results are deterministic: the same inputs give bit-identical outputs.
@@ -54,12 +56,12 @@ extern "C" {
  * [expert_offset[e], expert_offset[e+1]) and the first expert_count[e] of them
  * hold its token-slots. */
 #define MOE_TILE_M 256
-#define MOE_MAX_EXPERTS 64
+#define MOE_MAX_EXPERTS 256
 
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,      /* bad argument: null/misaligned pointer, bad size */
-  MOE_ENOTSUP = 2,     /* valid but unsupported shape (e.g. n_experts > 64) */
+  MOE_ENOTSUP = 2,     /* valid but unsupported shape (e.g. n_experts > 256) */
   MOE_EWORKSPACE = 3,  /* workspace missing or smaller than moe_workspace_bytes */
   MOE_EHIP = 4         /* a HIP launch failed */
 } moe_status_t;
@@ -77,7 +79,7 @@ typedef struct {
   int32_t tokens;     /* T >= 0 */
   int32_t dim;        /* D, multiple of 8 */
   int32_t hidden;     /* H, multiple of 8 */
-  int32_t n_experts;  /* n, 1..64 */
+  int32_t n_experts;  /* n, 1..MOE_MAX_EXPERTS (256) */
   int32_t top_k;      /* K, 1..n */
   int32_t out_dtype;  /* moe_dtype_t of the layer output `out` */
   int32_t path;       /* moe_path_t: which expert-product kernels to use */
@@ -103,10 +105,15 @@ const char* moe_status_string(int32_t status);
  *                                   ties to the lower index
  *   topk_gate fp32 [T][K]      out: softmax over the K kept logits
  *   logits    fp32 [T][n]      out, optional (NULL to skip)
- * Logits accumulate in fp32. */
+ *   ws, ws_bytes               scratch of moe_route_workspace_bytes(p) bytes
+ *                              (NULL/0 when that is 0; else MOE_EWORKSPACE)
+ * Logits accumulate in fp32.  With more than 16 experts they are computed on
+ * the matrix cores in contraction slices whose partial sums pass through ws
+ * and are added in slice order. */
+size_t moe_route_workspace_bytes(const moe_problem_t* p);
 moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate,
-                       int32_t* topk_idx, float* topk_gate, float* logits,
-                       void* stream);
+                       int32_t* topk_idx, float* topk_gate, float* logits, void* ws,
+                       size_t ws_bytes, void* stream);
 
 /* Group token-slots by expert (the "skip experts whose gate is zero" step of
  * section 2.1: each expert sees only the tokens routed to it, in unequal

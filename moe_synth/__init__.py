@@ -93,6 +93,13 @@ WORKLOADS = {
                        note="Mixtral shape, ~60% of token-slots on experts 0 and 1"),
     "large": Workload("large", 5, 32768, 4096, 14336, 8, 2, 1002, chunk=8192,
                       note="Mixtral shape, 32768 tokens streamed as 4 x 8192"),
+    # Fine-grained layout: 8 of 160 experts.  The expert width is not given;
+    # 768 keeps the layer's expert parameters near Mixtral's (160 * 768 vs
+    # 8 * 14336), rounded up to a multiple of 128 columns.
+    "fine_prefill": Workload("fine_prefill", 6, 4096, 4096, 768, 160, 8, 1006,
+                             note="fine-grained, 8 of 160 experts of width 768, 4096 tokens"),
+    "fine_decode": Workload("fine_decode", 7, 16, 4096, 768, 160, 8, 1006,
+                            note="fine-grained, 8 of 160 experts of width 768, 16 tokens"),
 }
 
 

@@ -26,9 +26,10 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
 TILE_M = 256
-MAX_EXPERTS = 64
+MAX_EXPERTS = 256
 
 EXPORTED = ("moe_capacity_rows", "moe_workspace_bytes", "moe_status_string", "moe_route",
+            "moe_route_workspace_bytes",
             "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
             "moe_decode_max_tokens", "moe_forward_timed", "moe_route_stats")
 
@@ -54,7 +55,9 @@ lib.moe_status_string.argtypes = [ctypes.c_int32]
 lib.moe_status_string.restype = ctypes.c_char_p
 lib.moe_decode_max_tokens.argtypes = []
 lib.moe_decode_max_tokens.restype = ctypes.c_int32
-lib.moe_route.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.moe_route_workspace_bytes.argtypes = [_P]
+lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
+lib.moe_route.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.moe_permute.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.moe_grouped_ffn.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.moe_combine.argtypes = [_P, _vp, _vp, _vp, _vp, _vp]
@@ -141,8 +144,15 @@ def _shape_of(x, w1, top_k, out_dtype=MOE_F32, path=PATH_AUTO) -> Problem:
     return problem(T, D, H, n, top_k, out_dtype, path)
 
 
-def route(x, w_gate, top_k: int, topk_idx=None, topk_gate=None, logits=None, stream=None):
-    """moe_route: returns (topk_idx int32 [T][K], topk_gate fp32 [T][K])."""
+def route_workspace_bytes(p: Problem) -> int:
+    return int(lib.moe_route_workspace_bytes(ctypes.byref(p)))
+
+
+def route(x, w_gate, top_k: int, topk_idx=None, topk_gate=None, logits=None, workspace=None,
+          stream=None):
+    """moe_route: returns (topk_idx int32 [T][K], topk_gate fp32 [T][K]).  The
+    scratch the router needs (more than 16 experts) is taken from `workspace`
+    or allocated here."""
     torch = _torch()
     T, D = x.shape
     n = w_gate.shape[1]
@@ -151,11 +161,17 @@ def route(x, w_gate, top_k: int, topk_idx=None, topk_gate=None, logits=None, str
         topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
     if topk_gate is None:
         topk_gate = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    need = route_workspace_bytes(p)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = _ptr(workspace, torch.uint8, None, "workspace", optional=True)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     _check("moe_route", lib.moe_route(
         ctypes.byref(p), _ptr(x, _bf16(), (T, D), "x"), _ptr(w_gate, _bf16(), (D, n), "w_gate"),
         _ptr(topk_idx, torch.int32, (T, top_k), "topk_idx"),
         _ptr(topk_gate, torch.float32, (T, top_k), "topk_gate"),
-        _ptr(logits, torch.float32, (T, n), "logits", optional=True), _stream(stream)))
+        _ptr(logits, torch.float32, (T, n), "logits", optional=True), ws_ptr, ws_bytes,
+        _stream(stream)))
     return topk_idx, topk_gate
 
 

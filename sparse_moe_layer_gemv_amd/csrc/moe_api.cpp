@@ -14,6 +14,9 @@ namespace {
 
 using moe::Shape;
 
+static_assert(moe::kMaxExperts == MOE_MAX_EXPERTS, "one expert limit for every kernel");
+static_assert(moe::kTileM == MOE_TILE_M, "one segment granule");
+
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -57,8 +60,10 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
 //   count     int32 [n]       offset    int32 [n+1]
 //   row_slot  int32 [cap]     slot_row  int32 [T*K]
 //   h         bf16  [cap][H]  y_rows    fp32  [2][cap][D] (split partials)
-// With the weight-streaming path (T <= kDecodeMaxTokens) the h region holds
-// the fp32 first-product results instead (decode_scratch_bytes).
+// With the weight-streaming path the h region holds the fp32 first-product
+// results instead (decode_scratch_bytes).  The router's partial logits
+// (route_scratch_bytes) use the start of the y_rows region, which is written
+// only after the router has finished with them.
 struct Carve {
   size_t idx, gate, count, offset, row_slot, slot_row, h, y, total;
 };
@@ -78,7 +83,9 @@ Carve carve(const Shape& s) {
   size_t h_bytes = size_t(s.cap) * s.H * 2;
   if (s.stream) h_bytes = std::max(h_bytes, moe::decode_scratch_bytes(s));
   c.h = o;        o = align_up(o + h_bytes, kAlign);
-  c.y = o;        o = align_up(o + size_t(kMaxSplits) * s.cap * s.D * 4, kAlign);
+  c.y = o;
+  o = align_up(o + std::max(size_t(kMaxSplits) * s.cap * s.D * 4, moe::route_scratch_bytes(s)),
+               kAlign);
   c.total = o;
   return c;
 }
@@ -151,19 +158,29 @@ const char* moe_status_string(int32_t status) {
 
 int32_t moe_decode_max_tokens(void) { return moe::kDecodeMaxTokens; }
 
+size_t moe_route_workspace_bytes(const moe_problem_t* p) {
+  Shape s;
+  if (check_problem(p, &s) != MOE_OK) return 0;
+  return moe::route_scratch_bytes(s);
+}
+
 moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate,
-                       int32_t* topk_idx, float* topk_gate, float* logits, void* stream) {
+                       int32_t* topk_idx, float* topk_gate, float* logits, void* ws,
+                       size_t ws_bytes, void* stream) {
   Shape s;
   moe_status_t st = check_problem(p, &s);
   if (st != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
   if (!x || !w_gate || !topk_idx || !topk_gate) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(topk_idx) || !aligned16(topk_gate) ||
-      (logits && !aligned16(logits)))
+      (logits && !aligned16(logits)) || (ws && !aligned16(ws)))
     return MOE_EINVAL;
+  const size_t need = moe::route_scratch_bytes(s);
+  if (need && (!ws || ws_bytes < need)) return MOE_EWORKSPACE;
   return hip_status(moe::launch_route(s, static_cast<const uint16_t*>(x),
                                       static_cast<const uint16_t*>(w_gate), topk_idx, topk_gate,
-                                      logits, static_cast<hipStream_t>(stream)));
+                                      logits, static_cast<float*>(ws),
+                                      static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* expert_count,
@@ -223,8 +240,6 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int3
                                         static_cast<hipStream_t>(stream)));
 }
 
-static_assert(moe::kMaxStatExperts >= MOE_MAX_EXPERTS, "histogram covers every expert");
-
 moe_status_t moe_route_stats(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
                              void* stream) {
   Shape s;
@@ -275,7 +290,7 @@ moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void
 
   if (mark(0) != hipSuccess) return MOE_EHIP;
   if (moe::launch_route(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
-                        idx, gate, nullptr, hs) != hipSuccess || mark(1) != hipSuccess)
+                        idx, gate, nullptr, y, hs) != hipSuccess || mark(1) != hipSuccess)
     return MOE_EHIP;
   if (moe::launch_permute(s, idx, count, offset, row_slot, slot_row, hs) != hipSuccess ||
       mark(2) != hipSuccess)

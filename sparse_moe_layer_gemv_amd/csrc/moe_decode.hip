@@ -32,25 +32,6 @@ namespace {
 constexpr int kUpWaves = 8;
 constexpr int kDownWaves = 16;
 
-__device__ __forceinline__ void transpose8x8_d(const uint4 (&in)[8], uint4 (&out)[8]) {
-  uint32_t w[8][4];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    w[j][0] = in[j].x; w[j][1] = in[j].y; w[j][2] = in[j].z; w[j][3] = in[j].w;
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = w[2 * p][c >> 1];
-      const uint32_t hi = w[2 * p + 1][c >> 1];
-      o[p] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    out[c] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
 // 8 consecutive h values of one token-slot: bf16(silu(a) * b) from the fp32
 // first-product results.
 __device__ __forceinline__ uint4 h_fragment(const float* a, const float* b) {
@@ -147,7 +128,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
       xv[g] = as_bf16x8(v);
     }
     uint4 op[8];
-    transpose8x8_d(wv, op);
+    transpose8x8_bf16(wv, op);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll

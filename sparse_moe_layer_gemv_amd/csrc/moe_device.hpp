@@ -31,6 +31,29 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// Transpose of an 8 x 8 block of bf16: in[j] holds row j (8 values, 16
+// bytes); out[c] gets column c, that is element c of every row, row j at
+// position j.  This turns 8 rows of a row-major [contraction][column] matrix
+// into the 8-deep contraction fragments a matrix-core operand takes per lane.
+__device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&out)[8]) {
+  uint32_t w[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    w[j][0] = in[j].x; w[j][1] = in[j].y; w[j][2] = in[j].z; w[j][3] = in[j].w;
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = w[2 * p][c >> 1];
+      const uint32_t hi = w[2 * p + 1][c >> 1];
+      o[p] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    out[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 // Butterfly sum over the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -162,6 +162,10 @@ __device__ __forceinline__ bf16x8 lds_read_wfrag(uint8_t* base, uint32_t off) {
 // once into that L2) and a few activation panels.
 //   offset: segment starts (tile-aligned), n experts, nu: column units per row
 //   tile.  Returns false for workgroups beyond the valid tiles.
+// Expert e's tiles are v in [nu*offset[e]/BM, nu*offset[e+1]/BM), so the
+// expert is the last e whose segment starts at or before v: a binary search
+// over the monotone offsets (empty experts share their start with the next
+// one, and the last of equal starts is the non-empty segment).
 __device__ __forceinline__ bool map_tile(int L, const int32_t* __restrict__ offset, int n,
                                          int nu, int& mt, int& unit, int& expert) {
   const int mt_count = offset[n] / BM;
@@ -170,20 +174,19 @@ __device__ __forceinline__ bool map_tile(int L, const int32_t* __restrict__ offs
   const int xcd = L & 7;
   const int local = L >> 3;
   const int q = total >> 3, rem = total & 7;
-  int v = xcd * q + min(xcd, rem) + local;
-  int m0 = 0;
-  for (int e = 0; e < n; ++e) {
-    const int me = (offset[e + 1] - offset[e]) / BM;
-    if (v < me * nu) {
-      mt = m0 + v % me;
-      unit = v / me;
-      expert = e;
-      return true;
-    }
-    v -= me * nu;
-    m0 += me;
+  const int v = xcd * q + min(xcd, rem) + local;
+  int lo = 0, hi = n - 1;  // invariant: the answer lies in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((offset[mid] / BM) * nu <= v) lo = mid; else hi = mid - 1;
   }
-  return false;  // not reached: v < total
+  const int m0 = offset[lo] / BM;
+  const int me = offset[lo + 1] / BM - m0;
+  const int vl = v - m0 * nu;
+  mt = m0 + vl % me;
+  unit = vl / me;
+  expert = lo;
+  return true;
 }
 
 // Per-lane state of one tile: DMA offsets and LDS read offsets.
@@ -620,9 +623,17 @@ hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* e
   return hipGetLastError();
 }
 
+// Splitting the second product's contraction in two doubles its tiles (for
+// few, large experts there are otherwise too few to fill the chip) but also
+// doubles the fp32 rows written here and read back by the combine.  So split
+// only when the expected tile count is low: rows ~ T*K plus half a padding
+// tile per expert, over the D / 128 column tiles.
 int grouped_down_splits(const Shape& s) {
   const int klen = s.H / 2;
-  return (s.H % (4 * BK) == 0 && klen >= 8 * BK && s.D % (2 * SUBN) == 0) ? 2 : 1;
+  if (!(s.H % (4 * BK) == 0 && klen >= 8 * BK && s.D % (2 * SUBN) == 0)) return 1;
+  const int64_t est_rows = int64_t(s.T) * s.K + int64_t(s.n) * BM / 2;
+  const int64_t est_tiles = (est_rows / BM) * (s.D / SUBN);
+  return est_tiles < 4096 ? 2 : 1;
 }
 
 hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, const uint16_t* h,

@@ -11,6 +11,8 @@ namespace moe {
 
 // Permuted-layout granule (rows per expert segment step); equals MOE_TILE_M.
 constexpr int kTileM = 256;
+// Largest number of experts; equals MOE_MAX_EXPERTS.
+constexpr int kMaxExperts = 256;
 // Largest T the weight-streaming (decode) expert path supports: every expert
 // then holds at most 64 token rows (4 groups of 16 per lane).
 constexpr int kStreamMaxTokens = 64;
@@ -27,8 +29,12 @@ struct Shape {
   bool stream;  // expert products by weight streaming (else tiled)
 };
 
+// Router and gate.  With more than 16 experts the logits run on the matrix
+// cores in contraction slices whose fp32 partial sums go through `scratch`
+// (route_scratch_bytes; 0 and unused otherwise).
+size_t route_scratch_bytes(const Shape& s);
 hipError_t launch_route(const Shape& s, const uint16_t* x, const uint16_t* w_gate,
-                        int32_t* topk_idx, float* topk_gate, float* logits,
+                        int32_t* topk_idx, float* topk_gate, float* logits, float* scratch,
                         hipStream_t stream);
 
 hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* expert_count,
@@ -71,7 +77,6 @@ hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_
                           bool out_bf16, hipStream_t stream);
 
 // Routing diagnostics: counts [2n + 2] (see moe_route_stats).
-constexpr int kMaxStatExperts = 64;
 hipError_t launch_route_stats(const Shape& s, const int32_t* topk_idx, int32_t* counts,
                               hipStream_t stream);
 

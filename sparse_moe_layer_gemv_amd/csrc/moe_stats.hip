@@ -22,8 +22,8 @@ constexpr int kStatThreads = 1024;
 // Expert ids outside [0, n) are not counted and match nothing.
 __global__ __launch_bounds__(kStatThreads) void route_stats_kernel(
     const int32_t* __restrict__ idx, int T, int K, int n, int32_t* __restrict__ counts) {
-  __shared__ int hist_first[kMaxStatExperts];
-  __shared__ int hist_any[kMaxStatExperts];
+  __shared__ int hist_first[kMaxExperts];
+  __shared__ int hist_any[kMaxExperts];
   __shared__ int rep[2];
   const int tid = threadIdx.x;
   for (int e = tid; e < n; e += kStatThreads) {

@@ -31,7 +31,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
+    for f in ("moe_route", "moe_route_workspace_bytes", "moe_permute", "moe_grouped_ffn",
+              "moe_combine", "moe_forward",
               "moe_workspace_bytes", "moe_capacity_rows", "moe_status_string",
               "moe_decode_max_tokens"):
         assert f in names
@@ -57,7 +58,8 @@ def test_capacity_and_workspace(moe):
     assert ws < cap * (14336 * 2 + 2 * 4096 * 4) + 4 * 1024 * 1024
     assert moe.capacity_rows(moe.problem(4096, 4096, 14336, 8, 9)) == -1   # K > n
     assert moe.workspace_bytes(moe.problem(16, 4100, 14336, 8, 2)) == 0    # dim % 8
-    assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 65, 2)) == 0   # n > 64
+    assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 257, 2)) == 0  # n > 256
+    assert moe.workspace_bytes(moe.problem(16, 4096, 768, 256, 8)) > 0     # n = 256
     assert moe.decode_max_tokens() >= 16
     # expert-product path: unknown values are invalid; forced streaming only up
     # to decode_max_tokens(); its scratch is part of the workspace
@@ -95,7 +97,7 @@ def test_validation_errors(moe):
     assert _fwd(moe, moe.problem(64, 128, 256, 8, 9)) == moe.MOE_EINVAL     # K > n
     assert _fwd(moe, moe.problem(64, 130, 256, 8, 2)) == moe.MOE_EINVAL     # dim % 8
     assert _fwd(moe, moe.problem(64, 128, 250, 8, 2)) == moe.MOE_EINVAL     # hidden % 8
-    assert _fwd(moe, moe.problem(64, 128, 256, 65, 2)) == moe.MOE_ENOTSUP   # n > 64
+    assert _fwd(moe, moe.problem(64, 128, 256, 257, 2)) == moe.MOE_ENOTSUP  # n > 256
     assert _fwd(moe, moe.problem(64, 128, 256, 8, 2, 7)) == moe.MOE_EINVAL  # out dtype
     assert _fwd(moe, good, {"x": 0}) == moe.MOE_EINVAL                      # null
     assert _fwd(moe, good, {"w1": FAKE + 8}) == moe.MOE_EINVAL              # misaligned
@@ -108,13 +110,22 @@ def test_validation_errors(moe):
 def test_stage_validation_errors(moe):
     p = moe.problem(64, 128, 256, 8, 2)
     L = moe.lib
-    assert L.moe_route(ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, None) == moe.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE + 4, None) == moe.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, None, 0, None) == moe.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE + 4, None, 0,
+                       None) == moe.MOE_EINVAL
+    # more than 16 experts: the matrix-core router needs its scratch
+    q = moe.problem(64, 128, 256, 160, 8)
+    assert moe.route_workspace_bytes(q) > 0
+    assert moe.route_workspace_bytes(p) == 0
+    assert L.moe_route(ctypes.byref(q), FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                       None) == moe.MOE_EWORKSPACE
+    assert L.moe_route(ctypes.byref(q), FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                       moe.route_workspace_bytes(q) - 1, None) == moe.MOE_EWORKSPACE
     assert L.moe_permute(ctypes.byref(p), FAKE, FAKE, FAKE, 0, FAKE, None) == moe.MOE_EINVAL
     assert L.moe_grouped_ffn(ctypes.byref(p), *([FAKE] * 8), FAKE, 16, None) == moe.MOE_EWORKSPACE
     assert L.moe_combine(ctypes.byref(p), FAKE, FAKE, FAKE, 0, None) == moe.MOE_EINVAL
     z = moe.problem(0, 128, 256, 8, 2)
-    assert L.moe_route(ctypes.byref(z), 0, 0, 0, 0, None, None) == moe.MOE_OK
+    assert L.moe_route(ctypes.byref(z), 0, 0, 0, 0, None, None, 0, None) == moe.MOE_OK
     assert L.moe_combine(ctypes.byref(z), 0, 0, 0, 0, None) == moe.MOE_OK
 
 

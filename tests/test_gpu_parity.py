@@ -66,6 +66,17 @@ SHAPES = [
     ("dense_k8", 300, 256, 384, 8, 8, 23),
     ("decode_dense_k8", 8, 256, 384, 8, 8, 24),
     ("k4_n32", 520, 256, 512, 32, 4, 25),
+    # many small experts (the fine-grained layout): matrix-core router, up to
+    # 256 experts, segments of a few rows each
+    ("fine_n160_k8", 600, 256, 256, 160, 8, 28),
+    ("fine_decode_t16", 16, 512, 256, 160, 8, 29),
+    ("fine_decode_t1", 1, 256, 128, 160, 8, 34),
+    ("n100_k6_ragged", 333, 200, 136, 100, 6, 30),
+    ("n130_k5", 250, 136, 128, 130, 5, 32),
+    ("n256_k8", 700, 384, 128, 256, 8, 31),
+    ("n24_k3", 300, 256, 256, 24, 3, 35),
+    # K = n = 96: slot selection runs past 64 slots per token
+    ("dense_n96", 40, 128, 64, 96, 96, 33),
 ]
 
 
@@ -93,10 +104,15 @@ def test_route_stage_and_logits(moe):
     assert rr.ok, rr
 
 
-def test_permute_stage_is_exact(moe):
-    rng = np.random.default_rng(5)
-    n, K = 8, 2
-    for T in (1, 63, 64, 65, 128, 1000, 5000, 9000):
+@pytest.mark.parametrize("n,K,Ts", [
+    (8, 2, (1, 63, 64, 65, 128, 1000, 5000, 9000)),
+    # many experts; P = 72000 slots puts two 1024-slot rounds in a workgroup
+    (160, 8, (1, 16, 127, 128, 4096, 9000)),
+    (256, 4, (3, 600, 20000)),
+], ids=["n8", "n160", "n256"])
+def test_permute_stage_is_exact(moe, n, K, Ts):
+    rng = np.random.default_rng(5 + n)
+    for T in Ts:
         idx = np.stack([rng.choice(n, size=K, replace=False) for _ in range(T)]).astype(np.int32)
         p = moe.problem(T, 8, 8, n, K)
         cap = moe.capacity_rows(p)
@@ -106,6 +122,34 @@ def test_permute_stage_is_exact(moe):
         assert np.array_equal(host(r["expert_offset"]), off)
         assert np.array_equal(host(r["row_slot"]), rs)
         assert np.array_equal(host(r["slot_row"]), sr)
+
+
+@pytest.mark.parametrize("n,D", [(8, 4096), (160, 4096), (100, 1000), (256, 512)])
+def test_route_stage_logits_large_n(moe, n, D):
+    import torch
+    T = 300
+    L = moe_synth.make_layer(T, D, 8, n, 8, seed=32 + n)
+    x, wg = dev_bf16(L.x), dev_bf16(L.w_gate)
+    logits = torch.empty((T, n), dtype=torch.float32, device="cuda:0")
+    idx, gate = moe.route(x, wg, 8, logits=logits)
+    ref = moe_ref.router_logits(L.x, L.w_gate)
+    assert np.abs(host(logits) - ref).max() < 2e-5
+    rr = parity.check_routing(ref, 8, host(idx), host(gate))
+    assert rr.ok, rr
+
+
+def test_route_ties_go_to_the_lower_index_with_many_experts(moe):
+    # W_g with duplicated columns gives exactly equal logits: the lower expert
+    # index must win every tie, slot order by decreasing logit
+    import torch
+    D, n, K, T = 256, 160, 8, 40
+    L = moe_synth.make_layer(T, D, 8, n, K, seed=77)
+    wg = L.w_gate.copy()
+    wg[:, 100:] = wg[:, :60]          # experts 100..159 copy experts 0..59
+    idx, gate = moe.route(dev_bf16(L.x), dev_bf16(wg), K)
+    ref = moe_ref.router_logits(L.x, wg)
+    want = moe_ref.topk_indices(ref, K)
+    assert np.array_equal(host(idx), want)
 
 
 def test_permute_drops_out_of_range_experts(moe):

@@ -1,6 +1,6 @@
 """GPU routing diagnostics (moe_route_stats) against the oracle's exact counts
 ("Mixtral of Experts", section 5): random and structured choice arrays, dropped
-ids, T = 0 and T = 1, n up to 64, and the router's own output on a Mixtral-shape
+ids, T = 0 and T = 1, n up to 256, and the router's own output on a Mixtral-shape
 workload.  Integer counts: bit-exact."""
 import numpy as np
 import pytest
@@ -38,6 +38,8 @@ CASES = [
     (777, 3, 6, 6, 0.1),
     (4096, 2, 64, 7, 0.0),
     (9000, 8, 64, 8, 0.05),
+    (4096, 8, 160, 9, 0.0),
+    (3000, 6, 256, 10, 0.02),
 ]
 
 
