@@ -54,6 +54,49 @@ __device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&
   }
 }
 
+// ---------------------------------------------------------------------------
+// Buffer resources and direct-to-LDS loads
+// ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond any resource (< 2^31 bytes): reads as 0
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data (gfx9 family)
+
+// s_waitcnt with the vector-memory counter limited to n and LDS operations
+// drained (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// s_waitcnt for this wave's LDS operations only (lgkmcnt 0; vmcnt and expcnt
+// left at their maxima).  A barrier does not wait for issued LDS reads, so a
+// stage must be drained this way before a barrier that lets other waves
+// overwrite it.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would wait for every outstanding DMA, including the ones meant to stay in
+// flight across the barrier.  Completion of the DMA that must be visible is
+// waited for explicitly (wait_vmcnt) before this.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ lds_u8* lds(uint8_t* p) { return (lds_u8*)(p); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
+}
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at dst + 16 * lane.
+// The range check applies to voff: an offset that must read as zero goes there.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, soff, 0, 0);
+}
+
 // Butterfly sum over the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -59,9 +59,6 @@
 namespace moe {
 namespace {
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
 constexpr int BM = 256;                       // rows (token-slots) per tile
 constexpr int BK = 32;                        // contraction depth of one step
 constexpr int SUBN = 128;                     // columns per weight sub-tile
@@ -78,8 +75,6 @@ constexpr int NB = 4;                         // weight stages (step s in stage 
 constexpr int A_DMA = A_BYTES / 1024 / NWAVES;  // 4 activation DMA instructions per wave per block
 constexpr int B_DMA = B_BYTES / 1024 / NWAVES;  // 2 weight DMA instructions per wave per stage
 constexpr int HALF_A = A_DMA / 2;
-constexpr uint32_t kOOB = 0x80000000u;        // buffer offset beyond any resource (< 2^31 bytes): reads as 0
-constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data (gfx9 family)
 
 static_assert(BM == kTileM, "segment granule must equal the row tile");
 static_assert(A_DMA == 4 && B_DMA == 2, "DMA split assumes 4 + 2 instructions per wave");
@@ -108,34 +103,6 @@ __device__ __forceinline__ uint8_t* b_stage() {
   else if constexpr (S == 1) return g_b1;
   else if constexpr (S == 2) return g_b2;
   else return g_b3;
-}
-
-// s_waitcnt with the vector-memory counter limited to n and LDS operations
-// drained (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads(): the fence
-// would wait for every outstanding DMA, including the ones meant to stay in
-// flight across the barrier.  Completion of the DMA that must be visible is
-// waited for explicitly (wait_vmcnt) before this.
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-__device__ __forceinline__ lds_u8* lds(uint8_t* p) { return (lds_u8*)(p); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
-}
-
-// 16 bytes per lane from buffer offset voff + soff into LDS at dst + 16 * lane.
-// The range check applies to voff: an offset that must read as zero goes there.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff,
-                                      uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
-                                           voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 lds_read128(const uint8_t* base, uint32_t off) {

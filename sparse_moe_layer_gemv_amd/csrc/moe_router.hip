@@ -135,21 +135,28 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 // Many experts (n > 16, up to the fine-grained layout).  The logits are then
 // a genuine matrix product, [T x D] . [D x n], and run on the matrix cores, in
 // two launches so that many workgroups share the reading of W_g even for a
-// handful of tokens.
+// handful of tokens: a first kernel writes fp32 partial logits per
+// contraction slice, [slice][token][expert]; router_select_kernel adds them.
 //
-// router_partial_kernel: a workgroup of 4 waves owns 16*RG tokens, 128
-// experts and one slice of the contraction; its waves take the slice's
-// 32-deep steps in turn.  Per step a lane loads an 8 x 8 block of W_g (8
-// contraction rows, 8 experts), transposes it in registers into 8 operands
-// whose rows are 16 experts strided by 8, and runs 8
-// v_mfma_f32_16x16x32_bf16 per 16-token group against that group's x
-// fragment.  The waves' sums are added in a fixed tree through LDS and the
-// slice's partial logits are written as fp32 rows [slice][token][expert].
+// router_ring_kernel (n a multiple of 4): a workgroup of 4 waves owns 64 or
+// 128 tokens (16 or 32 per wave) and one contraction slice.  The slice's 32-deep steps
+// of W_g (32 consecutive rows: one contiguous byte range) and of x pass
+// through a ring of kRingStages LDS stages filled by direct-to-LDS loads,
+// issued kRingStages-1 steps ahead.  Per step a wave reads its x fragment
+// (the A operand: 16 tokens x 32) and, per 16 experts, two transposing reads
+// of the W_g rows (16 experts x 32), one v_mfma_f32_16x16x32_bf16 per 16
+// tokens, W_g as the A operand so that a lane's results are 4 consecutive
+// experts of one token, stored as one 16-byte write.  Each wave's tokens are its own, so
+// no reduction across waves is needed.
 //
-// router_select_kernel: one wave per token adds the slices' partials in
-// slice order (deterministic), then selects the top K: each lane holds the
-// logits of experts lane, lane+64, ... and a butterfly argmax (larger value,
-// then lower index) picks each slot in turn.
+// router_partial_kernel (any n): the same split with per-lane loads of 8 x 8
+// W_g blocks transposed in registers, for widths whose rows are not 8-byte
+// aligned.
+//
+// router_select_kernel: 16 lanes per token add the slices' partials in slice
+// order (deterministic), then select the top K: each lane holds the logits of
+// 4 consecutive experts per 64, and a butterfly argmax over the 16 lanes
+// (larger value, then lower index) picks each slot in turn.
 constexpr int kRpWaves = 4;
 constexpr int kRpThreads = kRpWaves * 64;
 constexpr int kRpCols = 128;      // experts per workgroup
@@ -297,85 +304,325 @@ __global__ __launch_bounds__(kRpThreads) void router_partial_kernel(
   }
 }
 
+constexpr int kRingWaves = 4;
+constexpr int kRingStages = 4;
+constexpr int kRingTarget = 256;  // workgroups to aim for
+constexpr int kRingMaxSlices = 16;  // the selection reads every slice's partials
+
+struct RingSplit {
+  int rg;     // 16-token groups per wave (1, or 2 above 64 tokens)
+  int tiles;  // token tiles of 16 * rg * kRingWaves
+  int S;      // contraction slices
+  int kc;     // slice length (a multiple of 32)
+};
+
+RingSplit ring_split(const Shape& s) {
+  RingSplit r;
+  r.rg = s.T > 16 * kRingWaves ? 2 : 1;
+  const int tok = 16 * r.rg * kRingWaves;
+  r.tiles = (s.T + tok - 1) / tok;
+  const int ksteps = (s.D + 31) / 32;
+  int S = (kRingTarget + r.tiles - 1) / r.tiles;
+  S = std::max(1, std::min({S, ksteps / kRingStages, kRingMaxSlices}));
+  const int steps = (ksteps + S - 1) / S;
+  r.kc = steps * 32;
+  r.S = (s.D + r.kc - 1) / r.kc;
+  return r;
+}
+
+// NT: 16-expert column tiles (even, >= n/16); RG: 16-token groups per wave,
+// each W_g fragment feeding RG matrix-core products; CW: 1 KiB W_g loads per
+// wave per stage (a stage holds 32 rows = 64*n bytes of W_g, padded to 4*CW
+// KiB, and RG KiB of x per wave).
+template <int NT, int RG>
+struct Ring {
+  static constexpr int CW = (NT + 3) / 4;
+  static constexpr int WB = CW * kRingWaves * 1024;  // W_g bytes per stage
+  static constexpr int XB = kRingWaves * RG * 1024;  // x bytes per stage
+  static constexpr int SB = WB + XB;
+  static constexpr int TOK = 16 * RG * kRingWaves;
+  static constexpr int WAIT = (kRingStages - 1) * (CW + RG);  // loads issued after a step's
+};
+static_assert(kRingStages == 4, "the stages are four distinct LDS objects");
+
+struct RingLane {
+  __amdgpu_buffer_rsrc_t rw, rx;
+  uint32_t row_bytes;  // 2 n
+  uint32_t b_off;      // transposing-read offset within a stage
+  int wave, lane, kbeg, kend, nsteps, wchunks;
+};
+
+// Step i of the slice into stage `st`.  Loads past the slice (issued to keep
+// the per-step load count uniform) and past the W_g piece read as zeros.  A
+// step never crosses the slice end except at D, where the rows read as zeros.
+template <int NT, int RG>
+__device__ __forceinline__ void ring_issue(const RingLane& c, const uint32_t (&x_lane)[RG],
+                                           uint8_t* st, int i) {
+  using R = Ring<NT, RG>;
+  const int g = c.lane >> 4;
+  const int kw = c.kbeg + 32 * i;
+  const bool live = i < c.nsteps;
+  const uint32_t wbase = uint32_t(kw) * c.row_bytes;
+#pragma unroll
+  for (int cc = 0; cc < R::CW; ++cc) {
+    const int j = c.wave + kRingWaves * cc;
+    dma16(c.rw, lds(st) + j * 1024, live && j < c.wchunks ? wbase + j * 1024 + c.lane * 16 : kOOB,
+          0);
+  }
+#pragma unroll
+  for (int u = 0; u < RG; ++u) {
+    const bool xin = live && x_lane[u] != kOOB && kw + 8 * g < c.kend;
+    dma16(c.rx, lds(st) + R::WB + (c.wave * RG + u) * 1024,
+          xin ? x_lane[u] + uint32_t(kw) * 2 : kOOB, 0);
+  }
+}
+
+template <int NT, int RG>
+__device__ __forceinline__ void ring_compute(const RingLane& c, uint8_t* st,
+                                             f32x4 (&acc)[RG][NT]) {
+  using R = Ring<NT, RG>;
+  bf16x8 a[RG];
+#pragma unroll
+  for (int u = 0; u < RG; ++u)
+    a[u] = as_bf16x8(
+        *reinterpret_cast<const uint4*>(st + R::WB + (c.wave * RG + u) * 1024 + c.lane * 16));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    const uint32_t off = c.b_off + uint32_t(32 * q);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds(st) + off));
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds(st) + off + 4 * c.row_bytes));
+    const bf16x8 b =
+        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    // W_g rows as the A operand and x as B: the product is [expert][token],
+    // so each lane ends with 4 consecutive experts of one token
+#pragma unroll
+    for (int u = 0; u < RG; ++u)
+      acc[u][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[u], acc[u][q], 0, 0, 0);
+  }
+}
+
+// One step: stage `cur` is computed while the loads of 3 steps later go into
+// stage `nxt` (the one computed in the previous step).
+template <int NT, int RG>
+__device__ __forceinline__ void ring_step(const RingLane& c, const uint32_t (&x_lane)[RG],
+                                          uint8_t* cur, uint8_t* nxt, int i,
+                                          f32x4 (&acc)[RG][NT]) {
+  wait_lgkmcnt0();                                   // this wave's reads of `nxt` are done
+  stage_barrier();                                   // ... and every other wave's
+  ring_issue<NT, RG>(c, x_lane, nxt, i + kRingStages - 1);
+  wait_vmcnt<Ring<NT, RG>::WAIT>();                  // this wave's loads of step i landed
+  stage_barrier();                                   // ... and every other wave's loads
+  ring_compute<NT, RG>(c, cur, acc);
+}
+
+template <int NT, int RG>
+__global__ __launch_bounds__(kRingWaves * 64) void router_ring_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T, int D, int n, int S,
+    int kc, float* __restrict__ part) {
+  using R = Ring<NT, RG>;
+  // four stage objects, so the compiler can tell the loads into one stage
+  // from the reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[R::SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[R::SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[R::SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[R::SB];
+
+  RingLane c;
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = c.lane >> 4;     // contraction group of 8 (A and B), row group of 4 (C)
+  const int j16 = c.lane & 15;   // token (A row) and expert (B and C column)
+  const int sl = blockIdx.x % S;
+  const int t0 = (blockIdx.x / S) * R::TOK + 16 * RG * c.wave;  // this wave's first token
+  c.kbeg = sl * kc;
+  c.kend = min(D, c.kbeg + kc);
+  c.nsteps = (c.kend - c.kbeg + 31) / 32;
+  c.row_bytes = uint32_t(n) * 2;
+  c.wchunks = (64 * n + 1023) / 1024;  // 1 KiB pieces of a step's W_g rows
+  c.rw = make_rsrc(wg, uint32_t(D) * c.row_bytes);
+  c.rx = make_rsrc(x, uint32_t(T) * uint32_t(D) * 2);
+  // rows 8g + (j16 >> 2) (+4 for the second read), columns 16q + 4 (j16 & 3) .. +4
+  c.b_off = uint32_t(8 * g + (j16 >> 2)) * c.row_bytes + uint32_t(4 * (j16 & 3)) * 2;
+  uint32_t x_lane[RG];
+#pragma unroll
+  for (int u = 0; u < RG; ++u) {
+    const int tok = t0 + 16 * u + j16;
+    x_lane[u] = tok < T ? (uint32_t(tok) * uint32_t(D) + 8 * g) * 2 : kOOB;
+  }
+
+  f32x4 acc[RG][NT];
+#pragma unroll
+  for (int u = 0; u < RG; ++u)
+#pragma unroll
+    for (int q = 0; q < NT; ++q) acc[u][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  ring_issue<NT, RG>(c, x_lane, st0, 0);
+  ring_issue<NT, RG>(c, x_lane, st1, 1);
+  ring_issue<NT, RG>(c, x_lane, st2, 2);
+  // whole rounds of four steps: steps past the slice read zero-filled stages
+  // and add exact zeros, and a branch-free loop body keeps the compiler's
+  // own load tracking from waiting for the whole ring
+  for (int i = 0; i < c.nsteps; i += 4) {
+    ring_step<NT, RG>(c, x_lane, st0, st3, i, acc);
+    ring_step<NT, RG>(c, x_lane, st1, st0, i + 1, acc);
+    ring_step<NT, RG>(c, x_lane, st2, st1, i + 2, acc);
+    ring_step<NT, RG>(c, x_lane, st3, st2, i + 3, acc);
+  }
+  wait_vmcnt<0>();  // the trailing zero-fill loads must land before the workgroup ends
+
+  // acc[u][q][r]: expert 16 q + 4 g + r of token t0 + 16 u + j16; n is a
+  // multiple of 4, so a lane's 4 experts are all inside or all outside
+#pragma unroll
+  for (int u = 0; u < RG; ++u) {
+    const int t = t0 + 16 * u + j16;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const int e = 16 * q + 4 * g;
+      if (t < T && e < n)
+        *reinterpret_cast<f32x4*>(part + (size_t(sl) * T + t) * n + e) = acc[u][q];
+    }
+  }
+}
+
+// (bv, bi) <- the better of itself and the lane R places further round its
+// 16-lane row: larger value, then lower index; bi < 0 marks "none".
+template <int R>
+__device__ __forceinline__ void row_argmax(float& bv, int& bi) {
+  constexpr int kRowRor = 0x120 + R;  // DPP row_ror:R
+  const float ov = __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(bv), kRowRor, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, kRowRor, 0xF, 0xF, false);
+  if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// 16 lanes per token, 16 tokens per 256-thread workgroup; lane j16 of a token
+// holds the logits of experts 64 m + 4 j16 + c (c = 0..3, m = 0..NM-1), read
+// as 16-byte vectors when n is a multiple of 4.
+template <int NM, bool VEC4>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int S, int T, int n, int K, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_gate, float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  // the slices' partials are loaded 16 slices at a time (64 loads in flight
-  // per lane) and added in slice order: p0 + p1 + p2 + ...
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 16) {
-    float pv[4][16];
+  const int j16 = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool tok_ok = t < T;
+  const int tc = tok_ok ? t : 0;  // every lane takes part in the shuffles
+  auto load4 = [&](int sl, int m) -> f32x4 {
+    const float* row = part + (size_t(sl) * T + tc) * n;
+    const int e = 64 * m + 4 * j16;
+    if constexpr (VEC4) {
+      return *reinterpret_cast<const f32x4*>(row + min(e, n - 4));
+    } else {
+      f32x4 r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int e = lane + 64 * j;
-        pv[j][u] = (e < n && s0 + u < S) ? part[(size_t(s0 + u) * T + t) * n + e] : 0.f;
-      }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (s0 + u < S) v[j] = (s0 + u == 0) ? pv[j][u] : v[j] + pv[j][u];
-  }
-  if (logits)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < n) logits[size_t(t) * n + e] = v[j];
+      for (int c = 0; c < 4; ++c) r[c] = row[min(e + c, n - 1)];
+      return r;
     }
-  // Top-K by repeated selection.  Within a lane the experts rise with j, so a
-  // strict ">" keeps the lower index; across lanes equal values go to the
-  // lower index.  Slot s's expert and e^(l - top) stay in lane s % 64.
-  bool taken[4] = {false, false, false, false};
-  int my_idx[4] = {0, 0, 0, 0};
-  float my_ex[4] = {0.f, 0.f, 0.f, 0.f};
+  };
+  // the slices' partials, loaded SB slices at a time and added in slice order
+  constexpr int SB = 8;
+  f32x4 v[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) v[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    f32x4 pv[SB][NM];
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) pv[u][m] = load4(min(s0 + u, S - 1), m);
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        if (s0 + u < S) v[m] = (s0 + u == 0) ? pv[u][m] : v[m] + pv[u][m];
+  }
+  if (logits && tok_ok)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 64 * m + 4 * j16 + c;
+        if (e < n) logits[size_t(t) * n + e] = v[m][c];
+      }
+  // Top-K by repeated selection.  Within a lane the experts rise with (m, c),
+  // so a strict ">" keeps the lower index; across the 16 lanes equal values
+  // go to the lower index.  Slot s's expert and e^(l - top) stay in lane
+  // s % 16.
+  uint32_t taken = 0;  // bit 4 m + c
+  int my_idx[16];
+  float my_ex[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    my_idx[q] = 0;
+    my_ex[q] = 0.f;
+  }
   float top = 0.f, sum = 0.f;
   for (int s = 0; s < K; ++s) {
     int bi = -1;
     float bv = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < n && !taken[j] && (bi < 0 || v[j] > bv)) {
-        bi = e;
-        bv = v[j];
-      }
-    }
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, 64);
-      const int oi = __shfl_xor(bi, m, 64);
-      if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
+      for (int c = 0; c < 4; ++c) {
+        const int e = 64 * m + 4 * j16 + c;
+        if (e < n && !((taken >> (4 * m + c)) & 1u) && (bi < 0 || v[m][c] > bv)) {
+          bi = e;
+          bv = v[m][c];
+        }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (bi == lane + 64 * j) taken[j] = true;
+    // all-reduce over the 16 lanes of a row by rotations of 8, 4, 2, 1 (the
+    // order (value, then lower index) is total, so any combining order gives
+    // the same winner); DPP moves, no LDS round trips
+    row_argmax<8>(bv, bi);
+    row_argmax<4>(bv, bi);
+    row_argmax<2>(bv, bi);
+    row_argmax<1>(bv, bi);
+    if (((bi >> 2) & 15) == j16) taken |= 1u << (4 * (bi >> 6) + (bi & 3));
     if (s == 0) top = bv;
     const float ex = __expf(bv - top);
     sum += ex;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (s == q * 64 + lane) {
+    for (int q = 0; q < 16; ++q)
+      if (s == 16 * q + j16) {
         my_idx[q] = bi;
         my_ex[q] = ex;
       }
   }
+  if (!tok_ok) return;
   const float inv = 1.f / sum;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int s = q * 64 + lane;
+  for (int q = 0; q < 16; ++q) {
+    const int s = 16 * q + j16;
     if (s < K) {
       topk_idx[size_t(t) * K + s] = my_idx[q];
       topk_gate[size_t(t) * K + s] = my_ex[q] * inv;
     }
   }
+}
+
+template <int NM>
+void launch_select_t(const Shape& s, int S, const float* part, int32_t* idx, float* gate,
+                     float* logits, hipStream_t stream) {
+  const dim3 grid((s.T + 15) / 16), block(256);
+  if (s.n % 4 == 0)
+    hipLaunchKernelGGL((router_select_kernel<NM, true>), grid, block, 0, stream, part, S, s.T, s.n,
+                       s.K, idx, gate, logits);
+  else
+    hipLaunchKernelGGL((router_select_kernel<NM, false>), grid, block, 0, stream, part, S, s.T,
+                       s.n, s.K, idx, gate, logits);
+}
+
+void launch_select(const Shape& s, int S, const float* part, int32_t* idx, float* gate,
+                   float* logits, hipStream_t stream) {
+  const int nm = (s.n + 63) / 64;  // 64-expert groups (4 per lane)
+  if (nm <= 1) launch_select_t<1>(s, S, part, idx, gate, logits, stream);
+  else if (nm <= 2) launch_select_t<2>(s, S, part, idx, gate, logits, stream);
+  else if (nm <= 3) launch_select_t<3>(s, S, part, idx, gate, logits, stream);
+  else launch_select_t<4>(s, S, part, idx, gate, logits, stream);
 }
 
 template <int RG, bool VEC>
@@ -402,12 +649,39 @@ hipError_t launch_router_t(const Shape& s, const uint16_t* x, const uint16_t* wg
   return hipGetLastError();
 }
 
+template <int NT>
+void launch_ring_t(const Shape& s, const RingSplit& r, const uint16_t* x, const uint16_t* wg,
+                   float* part, hipStream_t stream) {
+  const dim3 grid(unsigned(r.tiles) * r.S), block(kRingWaves * 64);
+  if (r.rg == 1)
+    hipLaunchKernelGGL((router_ring_kernel<NT, 1>), grid, block, 0, stream, x, wg, s.T, s.D, s.n,
+                       r.S, r.kc, part);
+  else
+    hipLaunchKernelGGL((router_ring_kernel<NT, 2>), grid, block, 0, stream, x, wg, s.T, s.D, s.n,
+                       r.S, r.kc, part);
+}
+
+void launch_ring(const Shape& s, const RingSplit& r, const uint16_t* x, const uint16_t* wg,
+                 float* part, hipStream_t stream) {
+  const int nt = (s.n + 31) / 32 * 2;  // 16-expert tiles, rounded up to even
+  switch (nt) {
+    case 2: launch_ring_t<2>(s, r, x, wg, part, stream); break;
+    case 4: launch_ring_t<4>(s, r, x, wg, part, stream); break;
+    case 6: launch_ring_t<6>(s, r, x, wg, part, stream); break;
+    case 8: launch_ring_t<8>(s, r, x, wg, part, stream); break;
+    case 10: launch_ring_t<10>(s, r, x, wg, part, stream); break;
+    case 12: launch_ring_t<12>(s, r, x, wg, part, stream); break;
+    case 14: launch_ring_t<14>(s, r, x, wg, part, stream); break;
+    default: launch_ring_t<16>(s, r, x, wg, part, stream); break;
+  }
+}
+
 }  // namespace
 
 size_t route_scratch_bytes(const Shape& s) {
   if (s.T == 0 || !uses_matrix_router(s)) return 0;
-  const RouterSplit r = router_split(s);
-  return size_t(r.S) * s.T * s.n * sizeof(float);
+  const int S = s.n % 4 == 0 ? ring_split(s).S : router_split(s).S;
+  return size_t(S) * s.T * s.n * sizeof(float);
 }
 
 hipError_t launch_route(const Shape& s, const uint16_t* x, const uint16_t* w_gate,
@@ -418,13 +692,19 @@ hipError_t launch_route(const Shape& s, const uint16_t* x, const uint16_t* w_gat
   if (s.n == 16) return launch_router_t<16, 2, true>(s, x, w_gate, topk_idx, topk_gate, logits, stream);
   if (s.n <= 8) return launch_router_t<8, 4, false>(s, x, w_gate, topk_idx, topk_gate, logits, stream);
   if (s.n <= 16) return launch_router_t<16, 2, false>(s, x, w_gate, topk_idx, topk_gate, logits, stream);
-  const RouterSplit r = router_split(s);
-  if (s.n % 8 == 0) launch_partial<true>(s, r, x, w_gate, scratch, stream);
-  else launch_partial<false>(s, r, x, w_gate, scratch, stream);
+  int S;
+  if (s.n % 4 == 0) {
+    const RingSplit r = ring_split(s);
+    S = r.S;
+    launch_ring(s, r, x, w_gate, scratch, stream);
+  } else {
+    const RouterSplit r = router_split(s);
+    S = r.S;
+    launch_partial<false>(s, r, x, w_gate, scratch, stream);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_select_kernel, dim3((s.T + 3) / 4), dim3(256), 0, stream, scratch, r.S,
-                     s.T, s.n, s.K, topk_idx, topk_gate, logits);
+  launch_select(s, S, scratch, topk_idx, topk_gate, logits, stream);
   return hipGetLastError();
 }
 

@@ -124,10 +124,13 @@ def test_permute_stage_is_exact(moe, n, K, Ts):
         assert np.array_equal(host(r["slot_row"]), sr)
 
 
-@pytest.mark.parametrize("n,D", [(8, 4096), (160, 4096), (100, 1000), (256, 512)])
-def test_route_stage_logits_large_n(moe, n, D):
+# n % 64 == 0 gives the slowest (bank-conflicting) transposing reads of W_g:
+# the case that shows a stage being refilled before every read of it is done
+@pytest.mark.parametrize("n,D,T", [(8, 4096, 300), (160, 4096, 300), (100, 1000, 300),
+                                   (256, 512, 300), (128, 384, 700), (192, 384, 64),
+                                   (192, 1024, 700), (224, 384, 200)])
+def test_route_stage_logits_large_n(moe, n, D, T):
     import torch
-    T = 300
     L = moe_synth.make_layer(T, D, 8, n, 8, seed=32 + n)
     x, wg = dev_bf16(L.x), dev_bf16(L.w_gate)
     logits = torch.empty((T, n), dtype=torch.float32, device="cuda:0")
