@@ -235,9 +235,19 @@ hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
                               const int32_t* expert_offset, const int32_t* row_slot,
                               const float* ab, const uint16_t* w2, float* y_rows, int nsplit,
                               ptrdiff_t split_stride, hipStream_t stream) {
-  return launch_decode_t<false, kDownWaves>(s, nullptr, ab, expert_count, expert_offset, row_slot,
-                                            w2, nullptr, y_rows, s.H, s.D, nsplit, split_stride,
-                                            stream);
+  // the most waves (up to kDownWaves) that still give each at least 4 of the
+  // 32-deep steps: a short contraction (small experts) over 16 waves would
+  // spend its time in the reduction
+  const int steps = (s.H + nsplit - 1) / nsplit / 32;
+  if (steps >= 4 * kDownWaves)
+    return launch_decode_t<false, kDownWaves>(s, nullptr, ab, expert_count, expert_offset,
+                                              row_slot, w2, nullptr, y_rows, s.H, s.D, nsplit,
+                                              split_stride, stream);
+  if (steps >= 4 * 8)
+    return launch_decode_t<false, 8>(s, nullptr, ab, expert_count, expert_offset, row_slot, w2,
+                                     nullptr, y_rows, s.H, s.D, nsplit, split_stride, stream);
+  return launch_decode_t<false, 4>(s, nullptr, ab, expert_count, expert_offset, row_slot, w2,
+                                   nullptr, y_rows, s.H, s.D, nsplit, split_stride, stream);
 }
 
 }  // namespace moe

@@ -50,7 +50,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
   __syncthreads();
 
-  // 1. histogram of the valid slots: all of them, and those before `first`
+  // 1. histogram of the valid slots: all of them, and those before `first`;
+  //    the thread keeps the value of slot `first + tid` (its slot in this
+  //    block's first round) so that round need not read it again
+  int own = -1;
   for (int s0 = 0; s0 < P; s0 += 4 * kPermThreads) {
     int e[4];
 #pragma unroll
@@ -61,6 +64,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int s = s0 + u * kPermThreads + tid;
+      if (s == first + tid) own = e[u];
       if (e[u] >= 0 && e[u] < n) {
         atomicAdd(&s_cnt[e[u]], 1);
         if (s < first) atomicAdd(&s_run[e[u]], 1);
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int s = base + tid;
     int e = -1;
     if (s < P) {
-      e = topk_idx[s];
+      e = base == first ? own : topk_idx[s];
       if (e < 0 || e >= n) {
         slot_row[s] = -1;
         e = -1;
