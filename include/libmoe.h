@@ -14,8 +14,9 @@
  *            with a non-zero gate (skipping zero gates is exact)
  *
  * Mixtral uses n = 8 experts and K = 2 (Table 1: dim 4096, hidden_dim 14336).
- * The same calls serve the "fine-grained" layout the ai360xpert.com summary
- * mentions (many much smaller experts, e.g. 8 of 160): n up to 256.
+ * The same calls serve the fine-grained layout the ai360xpert.com summary
+ * mentions (a token picks, for instance, 8 of 160 far narrower experts): n up
+ * to 256.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
