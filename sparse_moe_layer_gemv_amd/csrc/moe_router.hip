@@ -188,7 +188,7 @@ RouterSplit router_split(const Shape& s) {
 
 bool uses_matrix_router(const Shape& s) { return s.n > 16; }
 
-template <int RG, bool VEC>
+template <int RG>
 __global__ __launch_bounds__(kRpThreads) void router_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T, int D, int n, int S,
     int kc, int cblocks, float* __restrict__ part) {
@@ -228,23 +228,16 @@ __global__ __launch_bounds__(kRpThreads) void router_partial_kernel(
   for (int k0 = kbeg + wave * 32; k0 < kend; k0 += kRpWaves * 32) {
     const int kk = k0 + kg * 8;
     const bool kval = kk < kend;  // kend is a multiple of 8: a group is all in or all out
+    // element-wise: W_g rows of these widths are not 16-byte aligned
     uint4 wv[8];
-    if constexpr (VEC) {
-      const bool ok = kval && col < n;  // n is a multiple of 8 here
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        wv[i] = ok ? *reinterpret_cast<const uint4*>(wg + size_t(kk + i) * n + col)
-                   : make_uint4(0, 0, 0, 0);
-    } else {
+    for (int i = 0; i < 8; ++i) {
+      uint32_t h[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t h[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          h[c] = (kval && col + c < n) ? uint32_t(wg[size_t(kk + i) * n + col + c]) : 0u;
-        wv[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                           h[6] | (h[7] << 16));
-      }
+      for (int c = 0; c < 8; ++c)
+        h[c] = (kval && col + c < n) ? uint32_t(wg[size_t(kk + i) * n + col + c]) : 0u;
+      wv[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                         h[6] | (h[7] << 16));
     }
     uint4 xv[RG];
 #pragma unroll
@@ -625,19 +618,18 @@ void launch_select(const Shape& s, int S, const float* part, int32_t* idx, float
   else launch_select_t<4>(s, S, part, idx, gate, logits, stream);
 }
 
-template <int RG, bool VEC>
+template <int RG>
 void launch_partial_t(const Shape& s, const RouterSplit& r, const uint16_t* x, const uint16_t* wg,
                       float* part, hipStream_t stream) {
   const unsigned blocks = unsigned(r.tiles) * r.cblocks * r.S;
-  hipLaunchKernelGGL((router_partial_kernel<RG, VEC>), dim3(blocks), dim3(kRpThreads), 0, stream,
-                     x, wg, s.T, s.D, s.n, r.S, r.kc, r.cblocks, part);
+  hipLaunchKernelGGL((router_partial_kernel<RG>), dim3(blocks), dim3(kRpThreads), 0, stream, x,
+                     wg, s.T, s.D, s.n, r.S, r.kc, r.cblocks, part);
 }
 
-template <bool VEC>
 void launch_partial(const Shape& s, const RouterSplit& r, const uint16_t* x, const uint16_t* wg,
                     float* part, hipStream_t stream) {
-  if (r.rg == 1) launch_partial_t<1, VEC>(s, r, x, wg, part, stream);
-  else launch_partial_t<2, VEC>(s, r, x, wg, part, stream);
+  if (r.rg == 1) launch_partial_t<1>(s, r, x, wg, part, stream);
+  else launch_partial_t<2>(s, r, x, wg, part, stream);
 }
 
 template <int NE, int TPW, bool VEC>
@@ -700,7 +692,7 @@ hipError_t launch_route(const Shape& s, const uint16_t* x, const uint16_t* w_gat
   } else {
     const RouterSplit r = router_split(s);
     S = r.S;
-    launch_partial<false>(s, r, x, w_gate, scratch, stream);
+    launch_partial(s, r, x, w_gate, scratch, stream);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
