@@ -141,7 +141,7 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx,
  *   expert_count  int32 [n], expert_offset int32 [n+1], row_slot int32 [cap]
  *                                 in: as written by moe_permute
  *   w1, w3 bf16 [n][D][H], w2 bf16 [n][H][D]   in
- *   y_rows        fp32 [cap][D]   out (rows of padding are written with zeros)
+ *   y_rows        fp32 [cap][D]   out (rows of padding are left as they were)
  *   ws, ws_bytes  workspace, >= moe_workspace_bytes(p)
  * The intermediate silu(a)*b is rounded once to bf16 (it is the input of the
  * second product); products accumulate in fp32. */

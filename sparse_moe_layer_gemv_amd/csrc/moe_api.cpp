@@ -122,8 +122,7 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
                                 y_part - y_rows, st);
   } else {
     *nsplit = y_part ? moe::grouped_down_splits(s) : 1;
-    e = moe::launch_grouped_down(s, offset, h, w2b, y_rows, *nsplit,
-                                 y_part - y_rows, st);
+    e = moe::launch_grouped_down(s, count, offset, h, w2b, y_rows, *nsplit, y_part - y_rows, st);
   }
   if (e != hipSuccess || (mark && mark(4) != hipSuccess)) return MOE_EHIP;
   return MOE_OK;

@@ -514,7 +514,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
 // last round of workgroups when the tile count is not a multiple of the CUs.
 template <bool EVEN>
 __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
-    const int32_t* __restrict__ expert_offset, const uint16_t* __restrict__ h,
+    const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
+    const uint16_t* __restrict__ h,
     const uint16_t* __restrict__ w2, float* __restrict__ y, int D, int H, int n, int nsplit,
     int klen, ptrdiff_t split_stride) {
   const int nt_count = (D + 2 * SUBN - 1) / (2 * SUBN);
@@ -551,10 +552,14 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
   set_klast(c, ksteps);
   run_tile<EVEN>(c, ksteps, wm, acc);
 
+  // rows past the expert's slots are padding: nothing reads them, so they
+  // are not written (no fp32 traffic for them)
+  const int rend = expert_offset[e] + expert_count[e];
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = row0 + wm * 128 + i * 32 + l32;
+    if (m >= rend) continue;
     float* yrow = y + size_t(m) * D;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -603,7 +608,8 @@ int grouped_down_splits(const Shape& s) {
   return est_tiles < 4096 ? 2 : 1;
 }
 
-hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, const uint16_t* h,
+hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
+                               const int32_t* expert_offset, const uint16_t* h,
                                const uint16_t* w2, float* y_rows, int nsplit, ptrdiff_t split_stride,
                                hipStream_t stream) {
   const int mt_max = int(s.cap / BM);
@@ -614,10 +620,10 @@ hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, con
   const bool even = (s.D % (2 * SUBN) == 0) && (klen % (2 * BK) == 0) && klen >= 4 * BK &&
                     klen * nsplit == s.H;
   if (even)
-    hipLaunchKernelGGL(grouped_down_kernel<true>, dim3(grid), dim3(NTHR), 0, stream,
+    hipLaunchKernelGGL(grouped_down_kernel<true>, dim3(grid), dim3(NTHR), 0, stream, expert_count,
                        expert_offset, h, w2, y_rows, s.D, s.H, s.n, nsplit, klen, split_stride);
   else
-    hipLaunchKernelGGL(grouped_down_kernel<false>, dim3(grid), dim3(NTHR), 0, stream,
+    hipLaunchKernelGGL(grouped_down_kernel<false>, dim3(grid), dim3(NTHR), 0, stream, expert_count,
                        expert_offset, h, w2, y_rows, s.D, s.H, s.n, 1, s.H, split_stride);
   return hipGetLastError();
 }

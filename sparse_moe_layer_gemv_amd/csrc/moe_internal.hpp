@@ -50,7 +50,9 @@ hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* e
 // partial sums: partial ks at y_rows + ks * split_stride (see
 // grouped_down_splits).
 int grouped_down_splits(const Shape& s);
-hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_offset, const uint16_t* h,
+// Rows past an expert's slots (padding) are not written.
+hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
+                               const int32_t* expert_offset, const uint16_t* h,
                                const uint16_t* w2, float* y_rows, int nsplit, ptrdiff_t split_stride,
                                hipStream_t stream);
 

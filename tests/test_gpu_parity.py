@@ -266,3 +266,40 @@ def test_stream_path_rejects_large_batches(moe):
         moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, path=moe.PATH_STREAM,
                     workspace=__import__("torch").empty(1 << 20, dtype=__import__("torch").uint8,
                                                         device="cuda:0"))
+
+
+@pytest.mark.parametrize("T,D,H,n,K", [(300, 256, 384, 8, 2), (16, 512, 1024, 8, 2),
+                                       (200, 256, 256, 160, 8)],
+                         ids=["tiled", "streaming", "n160_matrix_router"])
+def test_forward_graph_capture_replays_match_eager(moe, T, D, H, n, K):
+    # Every stage only enqueues kernels on the caller's stream (no host reads,
+    # no allocation, no memset nodes), so moe_forward can be captured into a
+    # HIP graph.  Each replay, with eager work and synchronisation between
+    # replays, must give the eager result bit for bit.
+    import torch
+    L = moe_synth.make_layer(T, D, H, n, K, seed=300 + T)
+    d = _upload(L)
+    p = moe.problem(T, D, H, n, K)
+    ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device="cuda:0")
+    args = (d["x"], d["wg"], d["w1"], d["w3"], d["w2"], K)
+    eager = host(moe.forward(*args, workspace=ws)).copy()
+    out = torch.empty((T, D), dtype=torch.float32, device="cuda:0")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the side stream, as torch asks before capture
+        moe.forward(*args, out=out, topk_idx=idx, topk_gate=gate, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(*args, out=out, topk_idx=idx, topk_gate=gate, workspace=ws)
+    for r in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)          # stale workspace contents must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = host(out)
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {r}"
