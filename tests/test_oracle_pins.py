@@ -252,6 +252,24 @@ def test_repetition_rates_match_random_assignment_closed_forms(golden):
     assert np.all(np.abs(share - cf["uniform_share"]) < 0.003)
 
 
+def test_repetition_rates_for_many_small_experts():
+    # The section-5 rates for K of n experts under random assignment: the next
+    # token's first choice matches with probability 1/n, and its K-set misses
+    # this token's K-set with probability C(n-K, K) / C(n, K) (both K-sets are
+    # uniform K-subsets).  n = 8, K = 2 gives the pages' 1/8 and 1 - (6/8)(5/7);
+    # here the fine-grained n = 160, K = 8.
+    assert math.isclose(1 - math.comb(6, 2) / math.comb(8, 2), 1 - (6 / 8) * (5 / 7))
+    n, K, N = 160, 8, 100000
+    rng = np.random.default_rng(16)
+    idx = moe_ref.topk_indices(rng.standard_normal((N, n)), K)
+    first, either = moe_ref.consecutive_repeat(idx)
+    want_either = 1 - math.comb(n - K, K) / math.comb(n, K)
+    assert abs(first - 1 / n) < 0.0015                            # ~6 sigma at N=1e5
+    assert abs(either - want_either) < 0.008
+    share = moe_ref.expert_share(idx, n)
+    assert np.all(np.abs(share - 1 / n) < 0.002)
+
+
 def test_repetition_rate_detects_structure():
     # pairs: (0,1)->(0,2) share first and an expert; (0,2)->(2,3) share expert 2
     # only; (2,3)->(4,5) nothing; (4,5)->(5,4) share experts but not the first
