@@ -264,7 +264,7 @@ def forward(x, w_gate, w1, w3, w2, top_k: int, out=None, topk_idx=None, topk_gat
 
     ``events``: optional sequence of 6 raw hipEvent_t handles; then
     moe_forward_timed records them between the stages.  ``path``: PATH_AUTO,
-    PATH_STREAM (weight streaming, T <= decode_max_tokens()) or PATH_TILED."""
+    PATH_STREAM (weight streaming, T <= 64) or PATH_TILED."""
     torch = _torch()
     p = _shape_of(x, w1, top_k, out_dtype, path)
     T, D, H, n = p.tokens, p.dim, p.hidden, p.n_experts

@@ -3,8 +3,9 @@
 // is the softmax of the Top-K logits of a linear layer; logits outside the
 // top K are set to -inf, so they get a gate of exactly zero.
 //
-// Up to 64 experts: a workgroup of 256 threads owns TPW consecutive tokens and splits the dim
-// axis between its threads: thread i reads the 16-byte steps 8*i + 2048*j, so
+// Up to 16 experts (router_kernel): a workgroup of 256 threads owns TPW
+// consecutive tokens and splits the dim axis between its threads: thread i
+// reads the 16-byte steps 8*i + 2048*j, so
 // each token row is read as coalesced 1 KiB segments, and every W_g row is
 // loaded once per step and reused for the TPW tokens.  The TPW*NE partial sums
 // of the 256 threads are reduced through LDS in two fixed-order stages (no
