@@ -133,15 +133,8 @@ __device__ __forceinline__ bf16x8 lds_read_wfrag(uint8_t* base, uint32_t off) {
 // expert is the last e whose segment starts at or before v: a binary search
 // over the monotone offsets (empty experts share their start with the next
 // one, and the last of equal starts is the non-empty segment).
-__device__ __forceinline__ bool map_tile(int L, const int32_t* __restrict__ offset, int n,
-                                         int nu, int& mt, int& unit, int& expert) {
-  const int mt_count = offset[n] / BM;
-  const int total = mt_count * nu;
-  if (L >= total) return false;
-  const int xcd = L & 7;
-  const int local = L >> 3;
-  const int q = total >> 3, rem = total & 7;
-  const int v = xcd * q + min(xcd, rem) + local;
+__device__ __forceinline__ void decode_tile(int v, const int32_t* __restrict__ offset, int n,
+                                            int nu, int& mt, int& unit, int& expert) {
   int lo = 0, hi = n - 1;  // invariant: the answer lies in [lo, hi]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -153,6 +146,17 @@ __device__ __forceinline__ bool map_tile(int L, const int32_t* __restrict__ offs
   mt = m0 + vl % me;
   unit = vl / me;
   expert = lo;
+}
+
+__device__ __forceinline__ bool map_tile(int L, const int32_t* __restrict__ offset, int n,
+                                         int nu, int& mt, int& unit, int& expert) {
+  const int mt_count = offset[n] / BM;
+  const int total = mt_count * nu;
+  if (L >= total) return false;
+  const int xcd = L & 7;
+  const int local = L >> 3;
+  const int q = total >> 3, rem = total & 7;
+  decode_tile(xcd * q + min(xcd, rem) + local, offset, n, nu, mt, unit, expert);
   return true;
 }
 
@@ -384,7 +388,7 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, int ksteps, int group
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-  if (!EVEN)
+  if (!EVEN || ksteps < 4)  // the ping-pong needs at least 4 steps (2 activation blocks)
     run_tile_simple<EVEN>(c, ksteps, acc);
   else if (group == 0)
     run_tile_pp<EVEN, 0>(c, ksteps, acc);
@@ -508,30 +512,23 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
 // ---------------------------------------------------------------------------
 // down: y = h w2
 // ---------------------------------------------------------------------------
-// The contraction (H) can be split into `nsplit` ranges of `klen` elements;
-// split ks writes its partial product to y + ks * split_stride, and the
-// partials are added (in split order) by the consumer.  This evens out the
-// last round of workgroups when the tile count is not a multiple of the CUs.
+// One tile: row tile mt of expert e, 256 output columns from n0, over
+// the contraction range [kbase, kbase + 32 * ksteps), stored to y for the
+// rows that hold slots (rows past the expert's slots are padding: nothing
+// reads them, so they are not written).
 template <bool EVEN>
-__global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
-    const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
-    const uint16_t* __restrict__ h,
-    const uint16_t* __restrict__ w2, float* __restrict__ y, int D, int H, int n, int nsplit,
-    int klen, ptrdiff_t split_stride) {
-  const int nt_count = (D + 2 * SUBN - 1) / (2 * SUBN);
-  int mt, unit, e;
-  if (!map_tile(blockIdx.x, expert_offset, n, nt_count * nsplit, mt, unit, e)) return;
-  const int nt = unit / nsplit;
-  const int ks = unit - nt * nsplit;
+__device__ __forceinline__ void down_tile(const int32_t* __restrict__ expert_count,
+                                          const int32_t* __restrict__ expert_offset,
+                                          const uint16_t* __restrict__ h,
+                                          const uint16_t* __restrict__ w2, float* y,
+                                          int D, int H, int mt, int n0, int e, int kbase,
+                                          int ksteps) {
   const int row0 = mt * BM;
-  const int n0 = nt * 2 * SUBN;
-  y += ks * split_stride;  // may point into another allocation (the workspace)
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   TileCtx c;
-  c.kbase = ks * klen;
+  c.kbase = kbase;
   c.ra = make_rsrc(h + size_t(row0) * H, uint32_t(BM) * H * 2);
   const size_t wsz = size_t(H) * D;
   c.rb = make_rsrc(w2 + size_t(e) * wsz, uint32_t(wsz * 2));
@@ -548,19 +545,15 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
   setup_reads(c, lane, wm, sub, cb);
 
   f32x16 acc[FM][FN];
-  const int ksteps = (min(klen, H - c.kbase) + BK - 1) / BK;
   set_klast(c, ksteps);
   run_tile<EVEN>(c, ksteps, wm, acc);
 
-  // rows past the expert's slots are padding: nothing reads them, so they
-  // are not written (no fp32 traffic for them)
   const int rend = expert_offset[e] + expert_count[e];
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = row0 + wm * 128 + i * 32 + l32;
     if (m >= rend) continue;
-    float* yrow = y + size_t(m) * D;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -569,11 +562,32 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
         if (!EVEN && col >= D) continue;
         f32x4 v = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
                    acc[i][j][q * 4 + 3]};
-        *reinterpret_cast<f32x4*>(yrow + col) = v;
+        *reinterpret_cast<f32x4*>(y + size_t(m) * D + col) = v;
       }
     }
   }
 }
+
+// The contraction (H) can be split into `nsplit` ranges of `klen` elements;
+// split ks writes its partial product to y + ks * split_stride, and the
+// partials are added (in split order) by the consumer.
+template <bool EVEN>
+__global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
+    const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2, float* __restrict__ y,
+    int D, int H, int n, int nsplit, int klen, ptrdiff_t split_stride) {
+  const int nt_count = (D + 2 * SUBN - 1) / (2 * SUBN);
+  int mt, unit, e;
+  if (!map_tile(blockIdx.x, expert_offset, n, nt_count * nsplit, mt, unit, e)) return;
+  const int nt = unit / nsplit;
+  const int ks = unit - nt * nsplit;
+  const int kbase = ks * klen;
+  const int ksteps = (min(klen, H - kbase) + BK - 1) / BK;
+  // y + ks * split_stride may point into another allocation (the workspace)
+  down_tile<EVEN>(expert_count, expert_offset, h, w2, y + ks * split_stride, D, H, mt,
+                  nt * 2 * SUBN, e, kbase, ksteps);
+}
+
 
 }  // namespace
 

@@ -77,6 +77,10 @@ SHAPES = [
     ("n24_k3", 300, 256, 256, 24, 3, 35),
     # K = n = 96: slot selection runs past 64 slots per token
     ("dense_n96", 40, 128, 64, 96, 96, 33),
+    # more tiles of the split second product than compute units, short
+    # contractions (4 and 6 activation blocks per half)
+    ("many_tiles_h256", 4096, 2048, 256, 8, 2, 36),
+    ("many_tiles_h384", 4000, 2048, 384, 8, 2, 37),
 ]
 
 
