@@ -488,23 +488,33 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
   run_tile<EVEN>(c, ksteps, wm, acc);
 
   // lane holds token row (wm*128 + 32 i + lane%32) and, per register quad q,
-  // 4 consecutive columns starting at 8 q + 4 (lane/32)
+  // 4 consecutive columns starting at 8 q + 4 (lane/32).  Lanes l and l+32
+  // hold the two halves of the same 8 columns; they swap one half so that the
+  // lower lane writes quads 0 and 2 and the upper lane quads 1 and 3, each as
+  // one 16-byte store (half the store instructions of 8-byte writes).
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = row0 + wm * 128 + i * 32 + l32;
     uint16_t* hrow = h + size_t(m) * H;
+    uint2 pk[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int col = n0 + wn * 32 + q * 8 + hi * 4;
-      if (!EVEN && col >= H) continue;
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = silu(acc[i][0][q * 4 + r]) * acc[i][1][q * 4 + r];
-      uint2 pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(hrow + col) = pk;
+      pk[q].x = pack_bf16x2(v[0], v[1]);
+      pk[q].y = pack_bf16x2(v[2], v[3]);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; qq += 2) {
+      const uint2 send = hi ? pk[qq] : pk[qq + 1];
+      const uint2 mine = hi ? pk[qq + 1] : pk[qq];
+      const uint32_t rx = __shfl_xor(send.x, 32, 64), ry = __shfl_xor(send.y, 32, 64);
+      const int col = n0 + wn * 32 + (qq + hi) * 8;
+      if (!EVEN && col >= H) continue;  // H is a multiple of 8: all 8 columns or none
+      *reinterpret_cast<uint4*>(hrow + col) =
+          hi ? make_uint4(rx, ry, mine.x, mine.y) : make_uint4(mine.x, mine.y, rx, ry);
     }
   }
 }
