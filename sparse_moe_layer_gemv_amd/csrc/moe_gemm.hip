@@ -53,6 +53,8 @@
 // a contiguous range of tiles ordered expert by expert, with an expert's
 // row-tiles consecutive, so the workgroups resident on one XCD share each
 // weight panel and a few activation panels in its L2.
+#include <algorithm>
+
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -448,74 +450,90 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
     const uint16_t* __restrict__ w3, uint16_t* __restrict__ h, int T, int D, int H, int n, int K,
     int k_shift) {
   const int nt_count = (H + SUBN - 1) / SUBN;
-  int mt, nt, e;
-  if (!map_tile(blockIdx.x, expert_offset, n, nt_count, mt, nt, e)) return;
-  const int row0 = mt * BM;
-  const int n0 = nt * SUBN;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  TileCtx c;
-  c.kbase = 0;
-  c.ra = make_rsrc(x, uint32_t(T) * D * 2);
-  const size_t wsz = size_t(D) * H;
-  c.rb = make_rsrc((b_sub_of_wave(wave) ? w3 : w1) + size_t(e) * wsz, uint32_t(wsz * 2));
-  // all row_slot loads first, then the token arithmetic (a branch around a
-  // division would serialise the loads)
+  // persistent: one workgroup per compute unit walks tiles L, L + G, ...
+  // (G a multiple of 8, so L stays on its XCD and the XCD's tile order is
+  // unchanged), without a workgroup launch between tiles; the next tile's
+  // mapping and row slots are read while this tile runs
+  int L = blockIdx.x;
+  int mt, nt, e;
+  if (!map_tile(L, expert_offset, n, nt_count, mt, nt, e)) return;
   int slot[A_DMA];
 #pragma unroll
-  for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[row0 + a_dma_row(wave, i, lane)];
-#pragma unroll
-  for (int i = 0; i < A_DMA; ++i) {
-    const uint32_t u = uint32_t(max(slot[i], 0));
-    const uint32_t tok = KPOW2 ? (u >> k_shift) : u / uint32_t(K);
-    const uint32_t off = tok * uint32_t(D) * 2 + a_dma_chunk(i, lane) * 16;
-    c.a_voff[i] = slot[i] >= 0 ? off : kOOB;
-  }
-  c.a_dst = wave * 32 * A_ROW;
-  setup_b_dma(c, lane, wave, n0, H);
-  // wave (wm, wn): rows wm*128 .. +128, columns wn*32 .. +32 of both w1
-  // (fragment 0) and w3 (fragment 1)
-  const int wm = wave >> 2, wn = wave & 3;
-  const int sub[FN] = {0, 1};
-  const int cb[FN] = {wn * 32, wn * 32};
-  setup_reads(c, lane, wm, sub, cb);
+  for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt * BM + a_dma_row(wave, i, lane)];
+  for (;;) {
+    const int row0 = mt * BM;
+    const int n0 = nt * SUBN;
+    int mt2 = 0, nt2 = 0, e2 = 0;
+    const bool more = map_tile(L + gridDim.x, expert_offset, n, nt_count, mt2, nt2, e2);
 
-  f32x16 acc[FM][FN];
-  const int ksteps = (D + BK - 1) / BK;
-  set_klast(c, ksteps);
-  run_tile<EVEN>(c, ksteps, wm, acc);
+    TileCtx c;
+    c.kbase = 0;
+    c.ra = make_rsrc(x, uint32_t(T) * D * 2);
+    const size_t wsz = size_t(D) * H;
+    c.rb = make_rsrc((b_sub_of_wave(wave) ? w3 : w1) + size_t(e) * wsz, uint32_t(wsz * 2));
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+      const uint32_t u = uint32_t(max(slot[i], 0));
+      const uint32_t tok = KPOW2 ? (u >> k_shift) : u / uint32_t(K);
+      const uint32_t off = tok * uint32_t(D) * 2 + a_dma_chunk(i, lane) * 16;
+      c.a_voff[i] = slot[i] >= 0 ? off : kOOB;
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt2 * BM + a_dma_row(wave, i, lane)];
+    }
+    c.a_dst = wave * 32 * A_ROW;
+    setup_b_dma(c, lane, wave, n0, H);
+    // wave (wm, wn): rows wm*128 .. +128, columns wn*32 .. +32 of both w1
+    // (fragment 0) and w3 (fragment 1)
+    const int wm = wave >> 2, wn = wave & 3;
+    const int sub[FN] = {0, 1};
+    const int cb[FN] = {wn * 32, wn * 32};
+    setup_reads(c, lane, wm, sub, cb);
 
-  // lane holds token row (wm*128 + 32 i + lane%32) and, per register quad q,
-  // 4 consecutive columns starting at 8 q + 4 (lane/32).  Lanes l and l+32
-  // hold the two halves of the same 8 columns; they swap one half so that the
-  // lower lane writes quads 0 and 2 and the upper lane quads 1 and 3, each as
-  // one 16-byte store (half the store instructions of 8-byte writes).
-  const int l32 = lane & 31, hi = lane >> 5;
+    f32x16 acc[FM][FN];
+    const int ksteps = (D + BK - 1) / BK;
+    set_klast(c, ksteps);
+    run_tile<EVEN>(c, ksteps, wm, acc);
+
+    // lane holds token row (wm*128 + 32 i + lane%32) and, per register quad q,
+    // 4 consecutive columns starting at 8 q + 4 (lane/32).  Lanes l and l+32
+    // hold the two halves of the same 8 columns; they swap one half so that the
+    // lower lane writes quads 0 and 2 and the upper lane quads 1 and 3, each as
+    // one 16-byte store (half the store instructions of 8-byte writes).
+    const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = row0 + wm * 128 + i * 32 + l32;
-    uint16_t* hrow = h + size_t(m) * H;
-    uint2 pk[4];
+    for (int i = 0; i < FM; ++i) {
+      const int m = row0 + wm * 128 + i * 32 + l32;
+      uint16_t* hrow = h + size_t(m) * H;
+      uint2 pk[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float v[4];
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = silu(acc[i][0][q * 4 + r]) * acc[i][1][q * 4 + r];
-      pk[q].x = pack_bf16x2(v[0], v[1]);
-      pk[q].y = pack_bf16x2(v[2], v[3]);
+        for (int r = 0; r < 4; ++r) v[r] = silu(acc[i][0][q * 4 + r]) * acc[i][1][q * 4 + r];
+        pk[q].x = pack_bf16x2(v[0], v[1]);
+        pk[q].y = pack_bf16x2(v[2], v[3]);
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4; qq += 2) {
+        const uint2 send = hi ? pk[qq] : pk[qq + 1];
+        const uint2 mine = hi ? pk[qq + 1] : pk[qq];
+        const uint32_t rx = __shfl_xor(send.x, 32, 64), ry = __shfl_xor(send.y, 32, 64);
+        const int col = n0 + wn * 32 + (qq + hi) * 8;
+        if (!EVEN && col >= H) continue;  // H is a multiple of 8: all 8 columns or none
+        *reinterpret_cast<uint4*>(hrow + col) =
+            hi ? make_uint4(rx, ry, mine.x, mine.y) : make_uint4(mine.x, mine.y, rx, ry);
+      }
     }
-#pragma unroll
-    for (int qq = 0; qq < 4; qq += 2) {
-      const uint2 send = hi ? pk[qq] : pk[qq + 1];
-      const uint2 mine = hi ? pk[qq + 1] : pk[qq];
-      const uint32_t rx = __shfl_xor(send.x, 32, 64), ry = __shfl_xor(send.y, 32, 64);
-      const int col = n0 + wn * 32 + (qq + hi) * 8;
-      if (!EVEN && col >= H) continue;  // H is a multiple of 8: all 8 columns or none
-      *reinterpret_cast<uint4*>(hrow + col) =
-          hi ? make_uint4(rx, ry, mine.x, mine.y) : make_uint4(mine.x, mine.y, rx, ry);
-    }
+    stage_barrier();  // every wave is past this tile's LDS use before the next tile's loads
+    if (!more) return;
+    L += gridDim.x;
+    mt = mt2;
+    nt = nt2;
+    e = e2;
   }
 }
 
@@ -599,6 +617,22 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
 }
 
 
+// One workgroup per compute unit (a multiple of 8, so that tile L + G stays
+// on the XCD of tile L); read once per device.
+int persistent_workgroups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+      cus = 256;
+    cached[dev] = cus / 8 * 8;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_offset,
@@ -606,8 +640,8 @@ hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* e
                              uint16_t* h, hipStream_t stream) {
   const int mt_max = int(s.cap / BM);
   const int nt = (s.H + SUBN - 1) / SUBN;
-  const int grid = mt_max * nt;
-  if (grid == 0) return hipSuccess;
+  if (mt_max * nt == 0) return hipSuccess;
+  const int grid = std::min(mt_max * nt, persistent_workgroups());
   const bool even = (s.H % SUBN == 0) && (s.D % (2 * BK) == 0) && s.D >= 4 * BK;
   // slot -> token is a shift when K is a power of two
   const bool pow2 = (s.K & (s.K - 1)) == 0;
