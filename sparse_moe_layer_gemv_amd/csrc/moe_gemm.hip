@@ -605,15 +605,28 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2, float* __restrict__ y,
     int D, int H, int n, int nsplit, int klen, ptrdiff_t split_stride) {
   const int nt_count = (D + 2 * SUBN - 1) / (2 * SUBN);
+  // persistent, as the first product: tiles L, L + G, ... of this XCD, the
+  // next tile's mapping read while the current one runs
+  int L = blockIdx.x;
   int mt, unit, e;
-  if (!map_tile(blockIdx.x, expert_offset, n, nt_count * nsplit, mt, unit, e)) return;
-  const int nt = unit / nsplit;
-  const int ks = unit - nt * nsplit;
-  const int kbase = ks * klen;
-  const int ksteps = (min(klen, H - kbase) + BK - 1) / BK;
-  // y + ks * split_stride may point into another allocation (the workspace)
-  down_tile<EVEN>(expert_count, expert_offset, h, w2, y + ks * split_stride, D, H, mt,
-                  nt * 2 * SUBN, e, kbase, ksteps);
+  if (!map_tile(L, expert_offset, n, nt_count * nsplit, mt, unit, e)) return;
+  for (;;) {
+    int mt2 = 0, unit2 = 0, e2 = 0;
+    const bool more = map_tile(L + gridDim.x, expert_offset, n, nt_count * nsplit, mt2, unit2, e2);
+    const int nt = unit / nsplit;
+    const int ks = unit - nt * nsplit;
+    const int kbase = ks * klen;
+    const int ksteps = (min(klen, H - kbase) + BK - 1) / BK;
+    // y + ks * split_stride may point into another allocation (the workspace)
+    down_tile<EVEN>(expert_count, expert_offset, h, w2, y + ks * split_stride, D, H, mt,
+                    nt * 2 * SUBN, e, kbase, ksteps);
+    stage_barrier();  // every wave is past this tile's LDS use before the next tile's loads
+    if (!more) return;
+    L += gridDim.x;
+    mt = mt2;
+    unit = unit2;
+    e = e2;
+  }
 }
 
 
@@ -672,8 +685,8 @@ hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
                                hipStream_t stream) {
   const int mt_max = int(s.cap / BM);
   const int nt = (s.D + 2 * SUBN - 1) / (2 * SUBN);
-  const int grid = mt_max * nt * nsplit;
-  if (grid == 0) return hipSuccess;
+  if (mt_max * nt * nsplit == 0) return hipSuccess;
+  const int grid = std::min(mt_max * nt * nsplit, persistent_workgroups());
   const int klen = s.H / nsplit;
   const bool even = (s.D % (2 * SUBN) == 0) && (klen % (2 * BK) == 0) && klen >= 4 * BK &&
                     klen * nsplit == s.H;
