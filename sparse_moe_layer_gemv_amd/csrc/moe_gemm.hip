@@ -306,17 +306,32 @@ __device__ __forceinline__ void tail_step(const TileCtx& c, int s0, int r, Frags
   if (r > I) step<EVEN, G, I>(c, s0 + I, f0, f1, acc);
 }
 
-// Main loop over the contraction (ksteps even, >= 4 steps of 32).
-template <bool EVEN, int G>
-__device__ __forceinline__ void run_tile_pp(const TileCtx& c, int ksteps, f32x16 (&acc)[FM][FN]) {
-  // prologue: every wave issues its share of weight steps 0..2 and activation
-  // blocks 0, 1 (steps 0..3); memory phase s then issues step s + 3 onwards
+// Prologue of the ping-pong: every wave issues its share of weight steps 0..2
+// and activation blocks 0, 1 (steps 0..3); memory phase s then issues step
+// s + 3 onwards.  The LDS must be free (every wave past its last reads).
+template <bool EVEN>
+__device__ __forceinline__ void pp_prologue(const TileCtx& c) {
   issue_b<EVEN>(c, b_stage<0>(), 0);
   issue_a<EVEN, 0, A_DMA>(c, a_block<0>(), 0);
   issue_b<EVEN>(c, b_stage<1>(), BK);
   issue_b<EVEN>(c, b_stage<2>(), 2 * BK);
   issue_a<EVEN, 0, A_DMA>(c, a_block<1>(), min(2 * BK, c.klast_a));
-  wait_vmcnt<2 * B_DMA + A_DMA>();  // weight step 0 and activation block 0 landed
+}
+
+// Main loop over the contraction (ksteps even, >= 4 steps of 32), after
+// pp_prologue.  A wave's vector-memory operations (loads, direct-to-LDS loads
+// and stores alike) complete in issue order, so the first wait counts the
+// operations the caller issued after the prologue: P_FIRST, or P_LATER when
+// `later` is set.
+template <bool EVEN, int G, int P_FIRST, int P_LATER>
+__device__ __forceinline__ void run_tile_pp_main(const TileCtx& c, int ksteps, bool later,
+                                                 f32x16 (&acc)[FM][FN]) {
+  // weight step 0 and activation block 0 landed (P_FIRST or P_LATER operations
+  // were issued after the prologue's loads)
+  if (later)
+    wait_vmcnt<2 * B_DMA + A_DMA + P_LATER>();
+  else
+    wait_vmcnt<2 * B_DMA + A_DMA + P_FIRST>();
   stage_barrier();
   Frags f0, f1;
   if (G == 0) {
@@ -354,6 +369,12 @@ __device__ __forceinline__ void run_tile_pp(const TileCtx& c, int ksteps, f32x16
   tail_step<EVEN, G, 10>(c, s, r, f0, f1, acc);
   // the surplus loads must land before the workgroup's LDS is released
   wait_vmcnt<0>();
+}
+
+template <bool EVEN, int G>
+__device__ __forceinline__ void run_tile_pp(const TileCtx& c, int ksteps, f32x16 (&acc)[FM][FN]) {
+  pp_prologue<EVEN>(c);
+  run_tile_pp_main<EVEN, G, 0, 0>(c, ksteps, false, acc);
 }
 
 // Any number of steps (ragged shapes): one activation block and one weight
@@ -452,57 +473,41 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
   const int nt_count = (H + SUBN - 1) / SUBN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // persistent: one workgroup per compute unit walks tiles L, L + G, ...
-  // (G a multiple of 8, so L stays on its XCD and the XCD's tile order is
-  // unchanged), without a workgroup launch between tiles; the next tile's
-  // mapping and row slots are read while this tile runs
-  int L = blockIdx.x;
-  int mt, nt, e;
-  if (!map_tile(L, expert_offset, n, nt_count, mt, nt, e)) return;
-  int slot[A_DMA];
-#pragma unroll
-  for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt * BM + a_dma_row(wave, i, lane)];
-  for (;;) {
-    const int row0 = mt * BM;
-    const int n0 = nt * SUBN;
-    int mt2 = 0, nt2 = 0, e2 = 0;
-    const bool more = map_tile(L + gridDim.x, expert_offset, n, nt_count, mt2, nt2, e2);
+  // wave (wm, wn): rows wm*128 .. +128, columns wn*32 .. +32 of both w1
+  // (fragment 0) and w3 (fragment 1)
+  const int wm = wave >> 2, wn = wave & 3;
+  const int sub[FN] = {0, 1};
+  const int cb[FN] = {wn * 32, wn * 32};
+  const int ksteps = (D + BK - 1) / BK;
+  const size_t wsz = size_t(D) * H;
 
+  auto make_ctx = [&](int nt_, int e_, const int (&sl)[A_DMA]) {
     TileCtx c;
     c.kbase = 0;
     c.ra = make_rsrc(x, uint32_t(T) * D * 2);
-    const size_t wsz = size_t(D) * H;
-    c.rb = make_rsrc((b_sub_of_wave(wave) ? w3 : w1) + size_t(e) * wsz, uint32_t(wsz * 2));
+    c.rb = make_rsrc((b_sub_of_wave(wave) ? w3 : w1) + size_t(e_) * wsz, uint32_t(wsz * 2));
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
-      const uint32_t u = uint32_t(max(slot[i], 0));
+      const uint32_t u = uint32_t(max(sl[i], 0));
       const uint32_t tok = KPOW2 ? (u >> k_shift) : u / uint32_t(K);
       const uint32_t off = tok * uint32_t(D) * 2 + a_dma_chunk(i, lane) * 16;
-      c.a_voff[i] = slot[i] >= 0 ? off : kOOB;
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt2 * BM + a_dma_row(wave, i, lane)];
+      c.a_voff[i] = sl[i] >= 0 ? off : kOOB;
     }
     c.a_dst = wave * 32 * A_ROW;
-    setup_b_dma(c, lane, wave, n0, H);
-    // wave (wm, wn): rows wm*128 .. +128, columns wn*32 .. +32 of both w1
-    // (fragment 0) and w3 (fragment 1)
-    const int wm = wave >> 2, wn = wave & 3;
-    const int sub[FN] = {0, 1};
-    const int cb[FN] = {wn * 32, wn * 32};
+    setup_b_dma(c, lane, wave, nt_ * SUBN, H);
     setup_reads(c, lane, wm, sub, cb);
-
-    f32x16 acc[FM][FN];
-    const int ksteps = (D + BK - 1) / BK;
     set_klast(c, ksteps);
-    run_tile<EVEN>(c, ksteps, wm, acc);
+    return c;
+  };
 
-    // lane holds token row (wm*128 + 32 i + lane%32) and, per register quad q,
-    // 4 consecutive columns starting at 8 q + 4 (lane/32).  Lanes l and l+32
-    // hold the two halves of the same 8 columns; they swap one half so that the
-    // lower lane writes quads 0 and 2 and the upper lane quads 1 and 3, each as
-    // one 16-byte store (half the store instructions of 8-byte writes).
+  // Epilogue: lane holds token row (wm*128 + 32 i + lane%32) and, per register
+  // quad q, 4 consecutive columns starting at 8 q + 4 (lane/32).  Lanes l and
+  // l+32 hold the two halves of the same 8 columns; they swap one half so that
+  // the lower lane writes quads 0 and 2 and the upper lane quads 1 and 3, each
+  // as one 16-byte store.  With EVEN shapes every lane issues all FM * 2 of
+  // them (kStoresPerWave), a count the next tile's first wait relies on.
+  constexpr int kStoresPerWave = FM * 2;
+  auto store_h = [&](const f32x16 (&acc)[FM][FN], int row0, int n0) {
     const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -528,12 +533,62 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
             hi ? make_uint4(rx, ry, mine.x, mine.y) : make_uint4(mine.x, mine.y, rx, ry);
       }
     }
-    stage_barrier();  // every wave is past this tile's LDS use before the next tile's loads
+  };
+
+  // Persistent: one workgroup per compute unit walks tiles L, L + G, ... (G a
+  // multiple of 8, so L stays on its XCD and the XCD's tile order is
+  // unchanged), without a workgroup launch between tiles.  The next tile's
+  // mapping and row slots are read while this tile runs, and (EVEN shapes)
+  // its prologue loads are issued before this tile's stores, so their latency
+  // hides behind the epilogue.  Per tile the wave issues, in this order: the
+  // row slots of the tile after next (A_DMA loads, always), the main loop,
+  // then the next tile's prologue and this tile's stores.
+  int L = blockIdx.x;
+  int mt, nt, e;
+  if (!map_tile(L, expert_offset, n, nt_count, mt, nt, e)) return;
+  int slot[A_DMA];
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt * BM + a_dma_row(wave, i, lane)];
+  TileCtx c = make_ctx(nt, e, slot);
+  if constexpr (EVEN) pp_prologue<true>(c);
+  bool later = false;
+  for (;;) {
+    int mt2 = 0, nt2 = 0, e2 = 0;
+    const bool more = map_tile(L + gridDim.x, expert_offset, n, nt_count, mt2, nt2, e2);
+    const int mt_load = more ? mt2 : mt;  // a valid tile when there is no next one
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt_load * BM + a_dma_row(wave, i, lane)];
+    asm volatile("" ::: "memory");
+
+    f32x16 acc[FM][FN];
+    if constexpr (EVEN) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+      if (wm == 0)
+        run_tile_pp_main<true, 0, A_DMA, kStoresPerWave + A_DMA>(c, ksteps, later, acc);
+      else
+        run_tile_pp_main<true, 1, A_DMA, kStoresPerWave + A_DMA>(c, ksteps, later, acc);
+    } else {
+      run_tile<EVEN>(c, ksteps, wm, acc);
+    }
+    stage_barrier();  // every wave is past this tile's LDS use
+    const int row0 = mt * BM, n0 = nt * SUBN;
+    if (more) {
+      c = make_ctx(nt2, e2, slot);
+      asm volatile("" ::: "memory");
+      if constexpr (EVEN) pp_prologue<true>(c);
+      asm volatile("" ::: "memory");
+    }
+    store_h(acc, row0, n0);
     if (!more) return;
     L += gridDim.x;
     mt = mt2;
     nt = nt2;
     e = e2;
+    later = true;
   }
 }
 
