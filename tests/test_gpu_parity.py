@@ -307,3 +307,57 @@ def test_forward_graph_capture_replays_match_eager(moe, T, D, H, n, K):
         torch.cuda.synchronize()
         got = host(out)
         assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {r}"
+
+
+@pytest.mark.parametrize("T,D,H,n,K", [(300, 256, 1024, 8, 2), (16, 512, 1024, 8, 2),
+                                       (200, 256, 256, 160, 8)],
+                         ids=["tiled_split", "streaming_split", "n160"])
+def test_stage_chain_matches_forward(moe, T, D, H, n, K):
+    # moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine gives moe_forward's
+    # output bit for bit (the stage path adds the split partials before the
+    # combine, the fused path inside it, in the same order)
+    import torch
+    L = moe_synth.make_layer(T, D, H, n, K, seed=400 + T)
+    d = _upload(L)
+    fwd = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], K)).copy()
+    idx, gate = moe.route(d["x"], d["wg"], K)
+    perm = moe.permute(idx, n)
+    y_rows = moe.grouped_ffn(d["x"], perm["expert_count"], perm["expert_offset"], perm["row_slot"],
+                             d["w1"], d["w3"], d["w2"], K)
+    out = host(moe.combine(y_rows, perm["slot_row"], gate))
+    assert np.array_equal(out.view(np.uint32), fwd.view(np.uint32))
+
+
+def test_forward_timed_events_bracket_the_stages(moe):
+    # moe_forward_timed: same result as moe_forward, and the 6 events it records
+    # are ordered, so the stage times are non-negative and add up
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(6):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    L = moe_synth.make_layer(500, 256, 512, 8, 2, seed=501)
+    d = _upload(L)
+    a = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2)).copy()
+    b = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, events=evs)).copy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    ms = []
+    for i in range(5):
+        t = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(evs[i]),
+                                       ctypes.c_void_p(evs[i + 1])) == 0
+        ms.append(t.value)
+    total = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(total), ctypes.c_void_p(evs[0]),
+                                   ctypes.c_void_p(evs[5])) == 0
+    assert all(m >= 0 for m in ms)
+    assert abs(sum(ms) - total.value) <= 1e-3 + 1e-3 * total.value
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
