@@ -319,19 +319,15 @@ __device__ __forceinline__ void pp_prologue(const TileCtx& c) {
 }
 
 // Main loop over the contraction (ksteps even, >= 4 steps of 32), after
-// pp_prologue.  A wave's vector-memory operations (loads, direct-to-LDS loads
-// and stores alike) complete in issue order, so the first wait counts the
-// operations the caller issued after the prologue: P_FIRST, or P_LATER when
-// `later` is set.
-template <bool EVEN, int G, int P_FIRST, int P_LATER>
-__device__ __forceinline__ void run_tile_pp_main(const TileCtx& c, int ksteps, bool later,
+// pp_prologue.  A wave's loads (plain and direct-to-LDS) complete in issue
+// order; LOADS_AFTER more loads were issued after the prologue's.  Stores may
+// also be pending; they only make the count stricter, so the wait below holds
+// whatever their order relative to the loads.
+template <bool EVEN, int G, int LOADS_AFTER>
+__device__ __forceinline__ void run_tile_pp_main(const TileCtx& c, int ksteps,
                                                  f32x16 (&acc)[FM][FN]) {
-  // weight step 0 and activation block 0 landed (P_FIRST or P_LATER operations
-  // were issued after the prologue's loads)
-  if (later)
-    wait_vmcnt<2 * B_DMA + A_DMA + P_LATER>();
-  else
-    wait_vmcnt<2 * B_DMA + A_DMA + P_FIRST>();
+  // weight step 0 and activation block 0 (the prologue's first 6 loads) landed
+  wait_vmcnt<2 * B_DMA + A_DMA + LOADS_AFTER>();
   stage_barrier();
   Frags f0, f1;
   if (G == 0) {
@@ -374,7 +370,7 @@ __device__ __forceinline__ void run_tile_pp_main(const TileCtx& c, int ksteps, b
 template <bool EVEN, int G>
 __device__ __forceinline__ void run_tile_pp(const TileCtx& c, int ksteps, f32x16 (&acc)[FM][FN]) {
   pp_prologue<EVEN>(c);
-  run_tile_pp_main<EVEN, G, 0, 0>(c, ksteps, false, acc);
+  run_tile_pp_main<EVEN, G, 0>(c, ksteps, acc);
 }
 
 // Any number of steps (ragged shapes): one activation block and one weight
@@ -504,9 +500,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
   // quad q, 4 consecutive columns starting at 8 q + 4 (lane/32).  Lanes l and
   // l+32 hold the two halves of the same 8 columns; they swap one half so that
   // the lower lane writes quads 0 and 2 and the upper lane quads 1 and 3, each
-  // as one 16-byte store.  With EVEN shapes every lane issues all FM * 2 of
-  // them (kStoresPerWave), a count the next tile's first wait relies on.
-  constexpr int kStoresPerWave = FM * 2;
+  // as one 16-byte store.
   auto store_h = [&](const f32x16 (&acc)[FM][FN], int row0, int n0) {
     const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -541,8 +535,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
   // mapping and row slots are read while this tile runs, and (EVEN shapes)
   // its prologue loads are issued before this tile's stores, so their latency
   // hides behind the epilogue.  Per tile the wave issues, in this order: the
-  // row slots of the tile after next (A_DMA loads, always), the main loop,
-  // then the next tile's prologue and this tile's stores.
+  // row slots of the tile after next (A_DMA loads, always, so the first wait
+  // of the main loop can count them), the main loop, then the next tile's
+  // prologue and this tile's stores.
   int L = blockIdx.x;
   int mt, nt, e;
   if (!map_tile(L, expert_offset, n, nt_count, mt, nt, e)) return;
@@ -551,7 +546,6 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
   for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt * BM + a_dma_row(wave, i, lane)];
   TileCtx c = make_ctx(nt, e, slot);
   if constexpr (EVEN) pp_prologue<true>(c);
-  bool later = false;
   for (;;) {
     int mt2 = 0, nt2 = 0, e2 = 0;
     const bool more = map_tile(L + gridDim.x, expert_offset, n, nt_count, mt2, nt2, e2);
@@ -568,9 +562,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
       if (wm == 0)
-        run_tile_pp_main<true, 0, A_DMA, kStoresPerWave + A_DMA>(c, ksteps, later, acc);
+        run_tile_pp_main<true, 0, A_DMA>(c, ksteps, acc);
       else
-        run_tile_pp_main<true, 1, A_DMA, kStoresPerWave + A_DMA>(c, ksteps, later, acc);
+        run_tile_pp_main<true, 1, A_DMA>(c, ksteps, acc);
     } else {
       run_tile<EVEN>(c, ksteps, wm, acc);
     }
@@ -588,7 +582,6 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
     mt = mt2;
     nt = nt2;
     e = e2;
-    later = true;
   }
 }
 
