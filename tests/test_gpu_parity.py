@@ -81,6 +81,9 @@ SHAPES = [
     # contractions (4 and 6 activation blocks per half)
     ("many_tiles_h256", 4096, 2048, 256, 8, 2, 36),
     ("many_tiles_h384", 4000, 2048, 384, 8, 2, 37),
+    # split second product over more than one round of tiles, the last round
+    # partly filled
+    ("split_rounds", 2200, 2048, 1024, 8, 2, 38),
 ]
 
 
