@@ -179,7 +179,11 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_ga
  * array of 6 hipEvent_t created by the caller; they are recorded on `stream`
  * before the router, after the router, after the permute, after the first
  * expert product (x.w1 / x.w3 with silu), after the second (.w2) and after the
- * combine.  The computation and its results are exactly those of moe_forward. */
+ * combine.  A NULL entry is skipped (each recorded event costs the stream a
+ * few microseconds, so a caller timing one stage records only its two).  On
+ * the weight-streaming path (T <= moe_decode_max_tokens()) there is no
+ * permute pass: event 2 directly follows event 1.  The computation and its
+ * results are exactly those of moe_forward. */
 moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void* w_gate,
                                const void* w1, const void* w3, const void* w2, void* out,
                                int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,

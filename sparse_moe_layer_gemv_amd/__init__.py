@@ -262,8 +262,8 @@ def forward(x, w_gate, w1, w3, w2, top_k: int, out=None, topk_idx=None, topk_gat
             path: int = PATH_AUTO):
     """moe_forward: the whole layer.  Returns out [T][D].
 
-    ``events``: optional sequence of 6 raw hipEvent_t handles; then
-    moe_forward_timed records them between the stages.  ``path``: PATH_AUTO,
+    ``events``: optional sequence of 6 raw hipEvent_t handles (None entries
+    are skipped); then moe_forward_timed records them between the stages.  ``path``: PATH_AUTO,
     PATH_STREAM (weight streaming, T <= 64) or PATH_TILED."""
     torch = _torch()
     p = _shape_of(x, w1, top_k, out_dtype, path)

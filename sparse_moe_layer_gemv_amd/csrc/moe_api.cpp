@@ -100,10 +100,13 @@ using MarkFn = std::function<hipError_t(int)>;
 
 // Expert products into y_rows (partial 0) and, when the second product is
 // split, y_part (partial 1); returns the number of partials in *nsplit.
+// With `topk_idx` (weight-streaming path only) the experts' token-slots are
+// read from the routing and the rows land at the slot index; otherwise the
+// permuted layout (count, offset, row_slot) gives them.
 moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const int32_t* offset,
-                     const int32_t* row_slot, const void* w1, const void* w3, const void* w2,
-                     float* y_rows, float* y_part, int* nsplit, uint16_t* h, hipStream_t st,
-                     const MarkFn& mark = nullptr) {
+                     const int32_t* row_slot, const int32_t* topk_idx, const void* w1,
+                     const void* w3, const void* w2, float* y_rows, float* y_part, int* nsplit,
+                     uint16_t* h, hipStream_t st, const MarkFn& mark = nullptr) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* w1b = static_cast<const uint16_t*>(w1);
   const uint16_t* w3b = static_cast<const uint16_t*>(w3);
@@ -111,14 +114,14 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   hipError_t e;
   float* ab = reinterpret_cast<float*>(h);  // decode: fp32 first products
   if (use_decode(s))
-    e = moe::launch_decode_up(s, xb, count, offset, row_slot, w1b, w3b, ab, st);
+    e = moe::launch_decode_up(s, xb, count, offset, row_slot, topk_idx, w1b, w3b, ab, st);
   else
     e = moe::launch_grouped_up(s, xb, offset, row_slot, w1b, w3b, h, st);
   if (e != hipSuccess || (mark && mark(3) != hipSuccess)) return MOE_EHIP;
   *nsplit = 1;
   if (use_decode(s)) {
     *nsplit = y_part ? moe::decode_down_splits(s) : 1;
-    e = moe::launch_decode_down(s, count, offset, row_slot, ab, w2b, y_rows, *nsplit,
+    e = moe::launch_decode_down(s, count, offset, row_slot, topk_idx, ab, w2b, y_rows, *nsplit,
                                 y_part - y_rows, st);
   } else {
     *nsplit = y_part ? moe::grouped_down_splits(s) : 1;
@@ -219,8 +222,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_
   int nsplit = 1;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   // the split partial is written y_part - y_rows floats after y_rows
-  st = run_ffn(s, x, expert_count, expert_offset, row_slot, w1, w3, w2, y_rows, y_part, &nsplit,
-               reinterpret_cast<uint16_t*>(base + c.h), hs);
+  st = run_ffn(s, x, expert_count, expert_offset, row_slot, nullptr, w1, w3, w2, y_rows, y_part,
+               &nsplit, reinterpret_cast<uint16_t*>(base + c.h), hs);
   if (st != MOE_OK || nsplit == 1) return st;
   return hip_status(moe::launch_add_rows(s, expert_offset, y_rows, y_part, hs));
 }
@@ -234,7 +237,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int3
   if (!y_rows || !slot_row || !topk_gate || !out) return MOE_EINVAL;
   if (!aligned16(y_rows) || !aligned16(slot_row) || !aligned16(topk_gate) || !aligned16(out))
     return MOE_EINVAL;
-  return hip_status(moe::launch_combine(s, y_rows, 1, 0, slot_row, topk_gate, out,
+  return hip_status(moe::launch_combine(s, y_rows, 1, 0, slot_row, nullptr, topk_gate, out,
                                         p->out_dtype == MOE_BF16,
                                         static_cast<hipStream_t>(stream)));
 }
@@ -284,22 +287,27 @@ moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void
   float* y = reinterpret_cast<float*>(base + c.y);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) {
-    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
+    return events && events[i] ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs)
+                               : hipSuccess;
   };
 
   if (mark(0) != hipSuccess) return MOE_EHIP;
   if (moe::launch_route(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
                         idx, gate, nullptr, y, hs) != hipSuccess || mark(1) != hipSuccess)
     return MOE_EHIP;
-  if (moe::launch_permute(s, idx, count, offset, row_slot, slot_row, hs) != hipSuccess ||
+  // The weight-streaming path finds each expert's token-slots in the routing
+  // itself (at most 64 tokens), so it needs no permute pass; its rows of y
+  // are then indexed by slot.
+  const bool scan = use_decode(s);
+  if ((!scan && moe::launch_permute(s, idx, count, offset, row_slot, slot_row, hs) != hipSuccess) ||
       mark(2) != hipSuccess)
     return MOE_EHIP;
   const size_t part_stride = size_t(s.cap) * s.D;
   int nsplit = 1;
-  st = run_ffn(s, x, count, offset, row_slot, w1, w3, w2, y, y + part_stride, &nsplit, h, hs,
-               events ? MarkFn(mark) : MarkFn());
+  st = run_ffn(s, x, count, offset, row_slot, scan ? idx : nullptr, w1, w3, w2, y,
+               y + part_stride, &nsplit, h, hs, events ? MarkFn(mark) : MarkFn());
   if (st != MOE_OK) return st;
-  if (moe::launch_combine(s, y, nsplit, part_stride, slot_row, gate, out,
+  if (moe::launch_combine(s, y, nsplit, part_stride, scan ? nullptr : slot_row, idx, gate, out,
                           p->out_dtype == MOE_BF16, hs) != hipSuccess ||
       mark(5) != hipSuccess)
     return MOE_EHIP;

@@ -25,6 +25,17 @@ __device__ __forceinline__ void store_out(void* out, size_t at, const f32x4& acc
   }
 }
 
+// Row of y_rows holding slot i: slot_row[i], or (slot_row null) the slot
+// itself when its expert index is in range; -1 when the slot contributes
+// nothing.
+__device__ __forceinline__ int slot_source(const int32_t* __restrict__ slot_row,
+                                           const int32_t* __restrict__ topk_idx, int n,
+                                           size_t i) {
+  if (slot_row) return slot_row[i];
+  const int e = topk_idx[i];
+  return (e >= 0 && e < n) ? int(i) : -1;
+}
+
 // One workgroup per (token, 1024-column block); each thread owns 4 columns.
 // The token's slots and gates are read once and all K (x nsplit partial) row
 // fragments are loaded before they are summed, so a small batch is one round
@@ -32,8 +43,8 @@ __device__ __forceinline__ void store_out(void* out, size_t at, const f32x4& acc
 template <bool OUT_BF16, int KMAX>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ y_rows, int nsplit, size_t split_stride,
-    const int32_t* __restrict__ slot_row, const float* __restrict__ gate, int D, int K, int ncb,
-    void* __restrict__ out) {
+    const int32_t* __restrict__ slot_row, const int32_t* __restrict__ topk_idx, int n,
+    const float* __restrict__ gate, int D, int K, int ncb, void* __restrict__ out) {
   const int t = blockIdx.x / ncb;
   const int d = (blockIdx.x - t * ncb) * kCols + threadIdx.x * 4;
   if (d >= D) return;
@@ -41,7 +52,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   float g[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
-    r[k] = k < K ? slot_row[size_t(t) * K + k] : -1;
+    r[k] = k < K ? slot_source(slot_row, topk_idx, n, size_t(t) * K + k) : -1;
     g[k] = k < K ? gate[size_t(t) * K + k] : 0.f;
   }
   f32x4 v[KMAX];
@@ -71,14 +82,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel_any_k(
     const float* __restrict__ y_rows, int nsplit, size_t split_stride,
-    const int32_t* __restrict__ slot_row, const float* __restrict__ gate, int D, int K, int ncb,
-    void* __restrict__ out) {
+    const int32_t* __restrict__ slot_row, const int32_t* __restrict__ topk_idx, int n,
+    const float* __restrict__ gate, int D, int K, int ncb, void* __restrict__ out) {
   const int t = blockIdx.x / ncb;
   const int d = (blockIdx.x - t * ncb) * kCols + threadIdx.x * 4;
   if (d >= D) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < K; ++k) {
-    const int r = slot_row[size_t(t) * K + k];
+    const int r = slot_source(slot_row, topk_idx, n, size_t(t) * K + k);
     if (r < 0) continue;
     const float g = gate[size_t(t) * K + k];
     f32x4 v = *reinterpret_cast<const f32x4*>(y_rows + size_t(r) * D + d);
@@ -94,32 +105,35 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel_any_k(
 
 template <bool OUT_BF16>
 hipError_t launch_combine_t(const Shape& s, const float* y_rows, int nsplit, size_t split_stride,
-                            const int32_t* slot_row, const float* topk_gate, void* out,
-                            hipStream_t stream) {
+                            const int32_t* slot_row, const int32_t* topk_idx,
+                            const float* topk_gate, void* out, hipStream_t stream) {
   const int ncb = (s.D + kCols - 1) / kCols;
   const dim3 grid(unsigned(s.T) * unsigned(ncb));
   if (s.K <= 2)
     hipLaunchKernelGGL((combine_kernel<OUT_BF16, 2>), grid, dim3(kCombineThreads), 0, stream,
-                       y_rows, nsplit, split_stride, slot_row, topk_gate, s.D, s.K, ncb, out);
+                       y_rows, nsplit, split_stride, slot_row, topk_idx, s.n, topk_gate, s.D, s.K,
+                       ncb, out);
   else if (s.K <= 8)
     hipLaunchKernelGGL((combine_kernel<OUT_BF16, 8>), grid, dim3(kCombineThreads), 0, stream,
-                       y_rows, nsplit, split_stride, slot_row, topk_gate, s.D, s.K, ncb, out);
+                       y_rows, nsplit, split_stride, slot_row, topk_idx, s.n, topk_gate, s.D, s.K,
+                       ncb, out);
   else
     hipLaunchKernelGGL((combine_kernel_any_k<OUT_BF16>), grid, dim3(kCombineThreads), 0, stream,
-                       y_rows, nsplit, split_stride, slot_row, topk_gate, s.D, s.K, ncb, out);
+                       y_rows, nsplit, split_stride, slot_row, topk_idx, s.n, topk_gate, s.D, s.K,
+                       ncb, out);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_t split_stride,
-                          const int32_t* slot_row, const float* topk_gate, void* out,
-                          bool out_bf16, hipStream_t stream) {
+                          const int32_t* slot_row, const int32_t* topk_idx,
+                          const float* topk_gate, void* out, bool out_bf16, hipStream_t stream) {
   if (s.T == 0) return hipSuccess;
-  return out_bf16 ? launch_combine_t<true>(s, y_rows, nsplit, split_stride, slot_row, topk_gate,
-                                           out, stream)
-                  : launch_combine_t<false>(s, y_rows, nsplit, split_stride, slot_row, topk_gate,
-                                            out, stream);
+  return out_bf16 ? launch_combine_t<true>(s, y_rows, nsplit, split_stride, slot_row, topk_idx,
+                                           topk_gate, out, stream)
+                  : launch_combine_t<false>(s, y_rows, nsplit, split_stride, slot_row, topk_idx,
+                                            topk_gate, out, stream);
 }
 
 __global__ __launch_bounds__(kCombineThreads) void add_rows_kernel(

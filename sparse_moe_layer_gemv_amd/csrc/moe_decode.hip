@@ -47,13 +47,19 @@ __device__ __forceinline__ uint4 h_fragment(const float* a, const float* b) {
 //       workgroup); out = ab fp32 [2][P][Ndim] (a at [0], b at [1], row = slot)
 // DOWN: ab rows through row_slot -> h; w = w2; out = y fp32 [cap][Ndim] + ks *
 //       split_stride (partial ks over contraction rows [ks*klen, +klen))
-template <bool UP, int RG, int WAVES>
+//
+// SCAN: the expert's token-slots are found by scanning the routing itself
+// (topk_idx, P = T*K entries, in slot order, so in the order the permute
+// would give them), and the second product writes its rows at the slot index
+// instead of the permuted row: no permute pass is needed.  Otherwise they come
+// from the permuted layout (expert_count, expert_offset, row_slot).
+template <bool UP, int RG, int WAVES, bool SCAN>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ ab,
     const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
-    const int32_t* __restrict__ row_slot, const uint16_t* __restrict__ w0,
-    const uint16_t* __restrict__ w1, void* __restrict__ out, int Kdim, int Ndim, int topk,
-    int P, int ncb, int nsplit, int klen, ptrdiff_t split_stride) {
+    const int32_t* __restrict__ row_slot, const int32_t* __restrict__ topk_idx,
+    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
+    int Kdim, int Ndim, int topk, int P, int ncb, int nsplit, int klen, ptrdiff_t split_stride) {
   constexpr int NACC = RG * 8;                     // f32x4 accumulators per lane
   constexpr int RED_SLOTS = WAVES / 2;
   __shared__ float red[RED_SLOTS * NACC * 4 * 64];
@@ -64,11 +70,33 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   const int r = blockIdx.x - e * per_e;
   const int sub = UP ? (r & 1) : (r % nsplit);     // UP: matrix; DOWN: split
   const int cb = UP ? (r >> 1) : (r / nsplit);
-  const int cnt = expert_count[e];
-  if (cnt == 0) return;
-  const int rbase = expert_offset[e];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  // SCAN: the expert's slots; every token holds an expert at most once, so
+  // there are at most T <= 64 of them
+  __shared__ int s_list[kStreamMaxTokens];
+  __shared__ int s_cnt;
+  int cnt, rbase = 0;
+  if constexpr (SCAN) {
+    if (wave == 0) {
+      int c = 0;
+      for (int base = 0; base < P; base += 64) {
+        const int i = base + lane;
+        const bool m = i < P && topk_idx[i] == e;
+        const uint64_t b = __ballot(m);
+        const int pos = c + __popcll(b & ((uint64_t(1) << lane) - 1));
+        if (m && pos < kStreamMaxTokens) s_list[pos] = i;
+        c += __popcll(b);
+      }
+      if (lane == 0) s_cnt = min(c, kStreamMaxTokens);
+    }
+    __syncthreads();
+    cnt = s_cnt;
+  } else {
+    cnt = expert_count[e];
+    rbase = expert_offset[e];
+  }
+  if (cnt == 0) return;
   const int n0 = cb * 128;
   const int kg = lane >> 4;
   const int nbk = lane & 15;
@@ -81,11 +109,20 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   const float* arow[RG];
   const float* brow[RG];
   bool aval[RG];
+  int slot_of[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     const int j = (lane & 15) + 16 * g;
     aval[g] = j < cnt;
-    const int slot = aval[g] ? row_slot[rbase + j] : 0;
+    int slot = 0;
+    if (aval[g]) {
+      if constexpr (SCAN) {
+        slot = s_list[j];
+      } else {
+        slot = row_slot[rbase + j];
+      }
+    }
+    slot_of[g] = slot;
     const int sl = slot >= 0 ? slot : 0;
     if (UP) {
       xrow[g] = x + size_t(sl / topk) * Kdim;
@@ -171,7 +208,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   for (int g = 0; g < RG; ++g) {
     if (!aval[g]) continue;
     const int j = (lane & 15) + 16 * g;
-    const size_t orow = UP ? size_t(sub) * P + row_slot[rbase + j] : size_t(rbase + j);
+    const size_t orow = UP ? size_t(sub) * P + slot_of[g]
+                           : (SCAN ? size_t(slot_of[g]) : size_t(rbase + j));
     float* op = static_cast<float*>(out) + (UP ? 0 : sub * split_stride) + orow * Ndim;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -185,30 +223,38 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   }
 }
 
+template <bool UP, int RG, int WAVES>
+void launch_decode_rg(const Shape& s, dim3 grid, const uint16_t* x, const float* ab,
+                      const int32_t* cnt, const int32_t* off, const int32_t* row_slot,
+                      const int32_t* topk_idx, const uint16_t* w0, const uint16_t* w1, void* out,
+                      int Kdim, int Ndim, int P, int ncb, int nsplit, int klen,
+                      ptrdiff_t split_stride, hipStream_t stream) {
+  auto kern = topk_idx ? decode_kernel<UP, RG, WAVES, true> : decode_kernel<UP, RG, WAVES, false>;
+  hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), 0, stream, x, ab, cnt, off, row_slot, topk_idx,
+                     w0, w1, out, Kdim, Ndim, s.K, P, ncb, nsplit, klen, split_stride);
+}
+
 template <bool UP, int WAVES>
 hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const float* ab, const int32_t* cnt,
-                           const int32_t* off, const int32_t* row_slot, const uint16_t* w0,
-                           const uint16_t* w1, void* out, int Kdim, int Ndim, int nsplit,
-                           ptrdiff_t split_stride, hipStream_t stream) {
+                           const int32_t* off, const int32_t* row_slot, const int32_t* topk_idx,
+                           const uint16_t* w0, const uint16_t* w1, void* out, int Kdim, int Ndim,
+                           int nsplit, ptrdiff_t split_stride, hipStream_t stream) {
   const int ncb = (Ndim + 127) / 128;
-  const int grid = s.n * ncb * (UP ? 2 : nsplit);
+  const dim3 grid(s.n * ncb * (UP ? 2 : nsplit));
   const int P = s.T * s.K;
   const int klen = (Kdim + nsplit - 1) / nsplit;
   // more token rows per lane means more accumulators: fewer waves, so the
   // registers fit without spilling
   static_assert(kStreamMaxTokens <= 4 * kDecodeRows, "four row groups per lane at most");
   if (s.T <= kDecodeRows)
-    hipLaunchKernelGGL((decode_kernel<UP, 1, WAVES>), dim3(grid), dim3(WAVES * 64), 0, stream, x,
-                       ab, cnt, off, row_slot, w0, w1, out, Kdim, Ndim, s.K, P, ncb, nsplit, klen,
-                       split_stride);
+    launch_decode_rg<UP, 1, WAVES>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                   Kdim, Ndim, P, ncb, nsplit, klen, split_stride, stream);
   else if (s.T <= 2 * kDecodeRows)
-    hipLaunchKernelGGL((decode_kernel<UP, 2, WAVES / 2>), dim3(grid), dim3(WAVES / 2 * 64), 0,
-                       stream, x, ab, cnt, off, row_slot, w0, w1, out, Kdim, Ndim, s.K, P, ncb,
-                       nsplit, klen, split_stride);
+    launch_decode_rg<UP, 2, WAVES / 2>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                       Kdim, Ndim, P, ncb, nsplit, klen, split_stride, stream);
   else
-    hipLaunchKernelGGL((decode_kernel<UP, 4, WAVES / 2>), dim3(grid), dim3(WAVES / 2 * 64), 0,
-                       stream, x, ab, cnt, off, row_slot, w0, w1, out, Kdim, Ndim, s.K, P, ncb,
-                       nsplit, klen, split_stride);
+    launch_decode_rg<UP, 4, WAVES / 2>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                       Kdim, Ndim, P, ncb, nsplit, klen, split_stride, stream);
   return hipGetLastError();
 }
 
@@ -225,29 +271,32 @@ int decode_down_splits(const Shape& s) {
 
 hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
                             const int32_t* expert_offset, const int32_t* row_slot,
-                            const uint16_t* w1, const uint16_t* w3, float* ab,
-                            hipStream_t stream) {
+                            const int32_t* topk_idx, const uint16_t* w1, const uint16_t* w3,
+                            float* ab, hipStream_t stream) {
   return launch_decode_t<true, kUpWaves>(s, x, nullptr, expert_count, expert_offset, row_slot,
-                                         w1, w3, ab, s.D, s.H, 1, 0, stream);
+                                         topk_idx, w1, w3, ab, s.D, s.H, 1, 0, stream);
 }
 
 hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
                               const int32_t* expert_offset, const int32_t* row_slot,
-                              const float* ab, const uint16_t* w2, float* y_rows, int nsplit,
-                              ptrdiff_t split_stride, hipStream_t stream) {
+                              const int32_t* topk_idx, const float* ab, const uint16_t* w2,
+                              float* y_rows, int nsplit, ptrdiff_t split_stride,
+                              hipStream_t stream) {
   // the most waves (up to kDownWaves) that still give each at least 4 of the
   // 32-deep steps: a short contraction (small experts) over 16 waves would
   // spend its time in the reduction
   const int steps = (s.H + nsplit - 1) / nsplit / 32;
   if (steps >= 4 * kDownWaves)
     return launch_decode_t<false, kDownWaves>(s, nullptr, ab, expert_count, expert_offset,
-                                              row_slot, w2, nullptr, y_rows, s.H, s.D, nsplit,
-                                              split_stride, stream);
+                                              row_slot, topk_idx, w2, nullptr, y_rows, s.H, s.D,
+                                              nsplit, split_stride, stream);
   if (steps >= 4 * 8)
-    return launch_decode_t<false, 8>(s, nullptr, ab, expert_count, expert_offset, row_slot, w2,
-                                     nullptr, y_rows, s.H, s.D, nsplit, split_stride, stream);
-  return launch_decode_t<false, 4>(s, nullptr, ab, expert_count, expert_offset, row_slot, w2,
-                                   nullptr, y_rows, s.H, s.D, nsplit, split_stride, stream);
+    return launch_decode_t<false, 8>(s, nullptr, ab, expert_count, expert_offset, row_slot,
+                                     topk_idx, w2, nullptr, y_rows, s.H, s.D, nsplit,
+                                     split_stride, stream);
+  return launch_decode_t<false, 4>(s, nullptr, ab, expert_count, expert_offset, row_slot,
+                                   topk_idx, w2, nullptr, y_rows, s.H, s.D, nsplit, split_stride,
+                                   stream);
 }
 
 }  // namespace moe

@@ -61,22 +61,29 @@ hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
 // `ab` ([2][T*K][H], decode_scratch_bytes); the second forms h = silu(a) * b
 // on the fly and may split its contraction into `nsplit` partial sums
 // (decode_down_splits), partial ks at y_rows + ks * split_stride.
+// Each expert's token-slots come from the permuted layout (expert_count,
+// expert_offset, row_slot; y rows at the permuted row) or, when topk_idx is
+// given, from scanning the routing (the others may be null; y rows at the
+// slot index t*K + k).
 size_t decode_scratch_bytes(const Shape& s);
 int decode_down_splits(const Shape& s);
 hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
                             const int32_t* expert_offset, const int32_t* row_slot,
-                            const uint16_t* w1, const uint16_t* w3, float* ab,
-                            hipStream_t stream);
+                            const int32_t* topk_idx, const uint16_t* w1, const uint16_t* w3,
+                            float* ab, hipStream_t stream);
 hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
                               const int32_t* expert_offset, const int32_t* row_slot,
-                              const float* ab, const uint16_t* w2, float* y_rows, int nsplit,
-                              ptrdiff_t split_stride, hipStream_t stream);
+                              const int32_t* topk_idx, const float* ab, const uint16_t* w2,
+                              float* y_rows, int nsplit, ptrdiff_t split_stride,
+                              hipStream_t stream);
 
 // out[t] = sum_k gate[t][k] * (sum_p y_rows[p * split_stride + row(t,k)]),
-// partials p summed first, in order.
+// partials p summed first, in order.  row(t,k) = slot_row[t*K + k] (-1: the
+// slot contributes nothing) or, with slot_row null, the slot index t*K + k
+// itself for slots whose topk_idx names an expert in [0, n).
 hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_t split_stride,
-                          const int32_t* slot_row, const float* topk_gate, void* out,
-                          bool out_bf16, hipStream_t stream);
+                          const int32_t* slot_row, const int32_t* topk_idx,
+                          const float* topk_gate, void* out, bool out_bf16, hipStream_t stream);
 
 // Routing diagnostics: counts [2n + 2] (see moe_route_stats).
 hipError_t launch_route_stats(const Shape& s, const int32_t* topk_idx, int32_t* counts,

@@ -362,5 +362,18 @@ def test_forward_timed_events_bracket_the_stages(moe):
                                    ctypes.c_void_p(evs[5])) == 0
     assert all(m >= 0 for m in ms)
     assert abs(sum(ms) - total.value) <= 1e-3 + 1e-3 * total.value
+    # null entries are skipped: only the two around the first expert product,
+    # on the tiled and on the weight-streaming path (which has no permute pass)
+    for T in (500, 16):
+        L = moe_synth.make_layer(T, 256, 512, 8, 2, seed=502 + T)
+        d = _upload(L)
+        a = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2)).copy()
+        part = [None, None, evs[2], evs[3], None, None]
+        b = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, events=part)).copy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        t = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(evs[2]),
+                                       ctypes.c_void_p(evs[3])) == 0
+        assert t.value > 0
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
