@@ -17,7 +17,7 @@ What it computes (sources are the pages on Mixtral of Experts):
 * Experts are SwiGLU blocks, K = 2, and y = sum_i Softmax(Top2(x W_g))_i *
   SwiGLU_i(x) -- same section, last display equation.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * SwiGLU_i(x) = (silu(x w1_i) * (x w3_i)) w2_i, silu(z) = z / (1 + e^-z),
   no biases; row-vector convention x . W, with W_g[D][n], w1/w3[D][H], w2[H][D].
