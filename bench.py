@@ -9,9 +9,9 @@ HBM.  Workloads (seeded, see moe_synth): prefill (T=4096, the default), decode
 fed as 4 chunks of 8192 through one workspace), tiny, and the fine-grained
 layout fine_prefill / fine_decode (8 of 160 experts of width 768, T=4096 / 16).
 
-Prints one JSON line.  The timed steps record HIP events on the layer's
-stream only around the dominant kernel (the first expert product: x.w1, x.w3
-+ silu), whose event-timed average launch the roofline object uses; the
+Prints one JSON line.  Every 4th timed step records HIP events on the
+layer's stream around the dominant kernel (the first expert product: x.w1,
+x.w3 + silu), whose event-timed average launch the roofline object uses; the
 per-stage breakdown comes from a separate pass with every stage boundary
 recorded (each recorded event costs the stream a few microseconds).
 The cpu_baseline object times the fp64 oracle on a bounded sample of the same
@@ -105,6 +105,8 @@ class HipEvents:
 
 
 STAGES = ("route", "permute", "up", "down", "combine")
+# the dominant kernel's launches are event-timed on every EVENT_EVERY-th timed step
+EVENT_EVERY = 4
 
 
 def log(*a):
@@ -256,12 +258,15 @@ def main(argv=None):
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
 
-    # Timed steps record only the two events around the first expert product
-    # (the dominant kernel the roofline needs, timed live); every recorded
-    # event costs the stream a few microseconds, so the other stage
-    # boundaries are taken in a separate pass afterwards.
-    up_evs = [[ev.create(2) for _ in range(n_chunks)] for _ in range(args.steps)]
-    timed = [[[None, None, e2[0], e2[1], None, None] for e2 in row] for row in up_evs]
+    # Every recorded event costs the stream a few microseconds, so the timed
+    # steps record only the two events around the first expert product (the
+    # dominant kernel, whose launches the roofline needs timed live), and only
+    # on every EVENT_EVERY-th step; the other stage boundaries are taken in a
+    # separate pass afterwards.
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    up_evs = {s: [ev.create(2) for _ in range(n_chunks)] for s in sampled}
+    timed = [[[None, None, e2[0], e2[1], None, None] for e2 in up_evs[s]] if s in up_evs else None
+             for s in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -269,7 +274,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"[bench] timed region done: {wall * 1e3:.2f} ms")
-    up_timed = [ev.elapsed_ms(e2[0], e2[1]) for row in up_evs for e2 in row]
+    up_timed = [ev.elapsed_ms(e2[0], e2[1]) for s in sampled for e2 in up_evs[s]]
 
     # stage breakdown: all six events, in a pass of its own
     prof_steps = max(1, min(args.steps, 10))
@@ -330,7 +335,8 @@ def main(argv=None):
                 "algorithmic_per_launch": per_launch_bytes, "traffic_unit": "HBM bytes per launch"}
     if per_launch_flops:
         roof["tflops"] = per_launch_flops / up_s / 1e12
-    roof["kernel_ms"] = up_avg_timed  # event-timed average launch over the timed steps
+    roof["kernel_ms"] = up_avg_timed  # event-timed average launch over the sampled timed steps
+    roof["kernel_launches_timed"] = len(up_timed)
 
     rec = {
         "metric": METRIC,
