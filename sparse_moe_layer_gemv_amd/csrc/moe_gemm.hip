@@ -661,8 +661,13 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
   for (;;) {
     int mt2 = 0, unit2 = 0, e2 = 0;
     const bool more = map_tile(L + gridDim.x, expert_offset, n, nt_count * nsplit, mt2, unit2, e2);
-    const int nt = unit / nsplit;
-    const int ks = unit - nt * nsplit;
+    // Units run contraction range by contraction range: the workgroups that
+    // one XCD runs together (several units x all row-tiles of an expert) then
+    // work on the same h columns for different output columns and share each
+    // h slice in L2.  With column-tile-major units they straddled both ranges,
+    // and the h re-fetches doubled.
+    const int ks = unit / nt_count;
+    const int nt = unit - ks * nt_count;
     const int kbase = ks * klen;
     const int ksteps = (min(klen, H - kbase) + BK - 1) / BK;
     // y + ks * split_stride may point into another allocation (the workspace)
