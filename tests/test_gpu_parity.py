@@ -266,6 +266,32 @@ def test_forced_expert_path(moe, T, path):
     assert orep.ok, orep
 
 
+@pytest.mark.parametrize("path", [1, 2], ids=["stream", "tiled"])
+def test_every_token_on_the_same_two_experts(moe, path):
+    # 64 copies of one token row: every token routes to the same two experts,
+    # so each of them holds all 64 slots (the most the streaming path takes
+    # per expert); every output row must equal the oracle's single-token result
+    import dataclasses
+    L = moe_synth.make_layer(64, 512, 1024, 8, 2, seed=95)
+    L = dataclasses.replace(L, x=np.repeat(L.x[:1], 64, axis=0))
+    d = _upload(L)
+    import torch
+    idx = torch.empty((64, 2), dtype=torch.int32, device="cuda:0")
+    gate = torch.empty((64, 2), dtype=torch.float32, device="cuda:0")
+    out = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, topk_idx=idx,
+                           topk_gate=gate, path=path))
+    idx_h = host(idx)
+    assert (idx_h == idx_h[:1]).all() and len(set(idx_h[0].tolist())) == 2
+    logits = moe_ref.router_logits(L.x[:1], L.w_gate)
+    rr = parity.check_routing(logits, 2, idx_h[:1], host(gate)[:1])
+    assert rr.ok, rr
+    ref = moe_ref.moe_layer(L.x[:1], L.w_gate, L.w1, L.w3, L.w2, 2, forced_idx=rr.forced_idx)
+    orep = parity.check_output(np.repeat(ref["y"], 64, axis=0), out)
+    assert orep.ok, orep
+    # identical tokens give identical rows, bit for bit
+    assert np.array_equal(out.view(np.uint32), np.repeat(out[:1], 64, axis=0).view(np.uint32))
+
+
 def test_stream_path_rejects_large_batches(moe):
     L = moe_synth.make_layer(65, 128, 256, 8, 2, seed=99)
     d = _upload(L)
