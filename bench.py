@@ -202,6 +202,83 @@ def crossover(args, torch, moe):
     return 0
 
 
+ROTATION_BYTES = 1 << 30  # inputs rotated per stage, so that every call reads from HBM
+
+
+def stages_alone(args, torch, moe):
+    """Router, permute and combine, each timed alone at a workload's shape.
+
+    The stage's large inputs are cycled through copies totalling at least
+    1 GiB (x for the router, the fp32 expert rows for the combine), far beyond
+    the 4 MiB L2 per XCD and the 256 MiB MALL, so the bytes a call reads come
+    from HBM.  Bytes per call are the algorithmic ones:
+      router:  T*D*2 (x) + D*n*2 (W_g) + T*K*8 (topk_idx, topk_gate)
+      permute: T*K*4 read; n*4 + (n+1)*4 + cap*4 + T*K*4 written
+      combine: T*K*D*4 (the token-slots' expert rows) + T*K*8 + T*D*4 (out)
+    Time per call is the hipEvent time of `steps` back-to-back calls on the
+    current stream, divided by `steps`.  Prints one JSON line."""
+    w = moe_synth.WORKLOADS[args.workload]
+    T, D, n, K = w.T, w.D, w.n, w.K
+    log(f"[stages] {args.workload}: T={T} D={D} n={n} K={K}")
+    xh, wgh = moe_synth.make_router_inputs(args.workload)
+    x0, wg = to_dev(xh), to_dev(wgh)
+    p = moe.problem(T, D, 8, n, K)
+    cap = moe.capacity_rows(p)
+    rws = torch.empty(max(moe.route_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda:0")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda:0")
+
+    def timed(fn, nbuf):
+        for i in range(min(args.warmup, nbuf) + 1):
+            fn(i % nbuf)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i % nbuf)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps * 1e3  # us per call
+
+    res = {}
+    # router over rotating copies of x
+    nx = max(1, -(-ROTATION_BYTES // (T * D * 2)))
+    xs = [x0.clone() for _ in range(nx)]
+    us = timed(lambda i: moe.route(xs[i], wg, K, topk_idx=idx, topk_gate=gate, workspace=rws), nx)
+    res["route"] = {"us": us, "bytes": T * D * 2 + D * n * 2 + T * K * 8, "rotated_bytes": nx * T * D * 2}
+    del xs
+    # permute: a few kilobytes in and out, so latency-bound; rotated copies of
+    # the routing all the same
+    ni = 64
+    idxs = [idx.clone() for _ in range(ni)]
+    outs = {"expert_count": torch.empty(n, dtype=torch.int32, device="cuda:0"),
+            "expert_offset": torch.empty(n + 1, dtype=torch.int32, device="cuda:0"),
+            "row_slot": torch.empty(cap, dtype=torch.int32, device="cuda:0"),
+            "slot_row": torch.empty(T * K, dtype=torch.int32, device="cuda:0")}
+    us = timed(lambda i: moe.permute(idxs[i], n, out=outs), ni)
+    res["permute"] = {"us": us, "bytes": T * K * 4 + (2 * n + 1) * 4 + cap * 4 + T * K * 4}
+    perm = moe.permute(idx, n)
+    # combine over rotating expert-row buffers (one fp32 partial, as moe_combine takes)
+    ny = max(1, -(-ROTATION_BYTES // (cap * D * 4)))
+    ys = [torch.empty((cap, D), dtype=torch.float32, device="cuda:0").uniform_(-1, 1)
+          for _ in range(ny)]
+    out = torch.empty((T, D), dtype=torch.float32, device="cuda:0")
+    us = timed(lambda i: moe.combine(ys[i], perm["slot_row"], gate, out=out), ny)
+    res["combine"] = {"us": us, "bytes": T * K * D * 4 + T * K * 8 + T * D * 4,
+                      "rotated_bytes": ny * cap * D * 4}
+    del ys
+    for r in res.values():
+        r["gbs"] = r["bytes"] / (r["us"] * 1e-6) / 1e9
+        r["hbm_frac"] = r["gbs"] / PEAK_HBM_GBS
+    rec = {"metric": "stage-alone time and HBM throughput (router, permute, combine)",
+           "unit": "GB/s", "data": "synthetic", "dtype": "bf16 in, fp32 out",
+           "config": {"workload": args.workload, "tokens": T, "dim": D, "n_experts": n,
+                      "top_k": K, "steps": args.steps},
+           "peak_hbm_gbs": PEAK_HBM_GBS, "stages": res}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +291,9 @@ def main(argv=None):
     ap.add_argument("--crossover", action="store_true",
                     help="small-batch sweep: time both expert-product paths for T = 1..256 and "
                          "print one JSON line with the measured crossover")
+    ap.add_argument("--stages", action="store_true",
+                    help="router, permute and combine each timed alone at the workload's shape, "
+                         "over rotating inputs of at least 1 GiB (one JSON line)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -228,6 +308,8 @@ def main(argv=None):
 
     if args.crossover:
         return crossover(args, torch, moe)
+    if args.stages:
+        return stages_alone(args, torch, moe)
 
     w = moe_synth.WORKLOADS[args.workload]
     T, D, H, n, K = w.T, w.D, w.H, w.n, w.K

@@ -133,7 +133,8 @@ def test_permute_stage_is_exact(moe, n, K, Ts):
 
 # n % 64 == 0 gives the slowest (bank-conflicting) transposing reads of W_g:
 # the case that shows a stage being refilled before every read of it is done
-@pytest.mark.parametrize("n,D,T", [(8, 4096, 300), (160, 4096, 300), (100, 1000, 300),
+@pytest.mark.parametrize("n,D,T", [(8, 4096, 300), (8, 4096, 2048), (16, 512, 2500),
+                                   (12, 256, 3000), (160, 4096, 300), (100, 1000, 300),
                                    (256, 512, 300), (128, 384, 700), (192, 384, 64),
                                    (192, 1024, 700), (224, 384, 200)])
 def test_route_stage_logits_large_n(moe, n, D, T):
