@@ -54,6 +54,7 @@
 // row-tiles consecutive, so the workgroups resident on one XCD share each
 // weight panel and a few activation panels in its L2.
 #include <algorithm>
+#include <atomic>
 
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
@@ -685,18 +686,21 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
 
 // One workgroup per compute unit (a multiple of 8, so that tile L + G stays
 // on the XCD of tile L); read once per device.
+// Host threads may race here; they all store the same value.
 int persistent_workgroups() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
+  int g = cached[dev].load(std::memory_order_relaxed);
+  if (g == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 8)
       cus = 256;
-    cached[dev] = cus / 8 * 8;
+    g = cus / 8 * 8;
+    cached[dev].store(g, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return g;
 }
 
 }  // namespace
