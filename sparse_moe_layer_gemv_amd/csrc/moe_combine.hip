@@ -13,15 +13,21 @@ namespace {
 constexpr int kCombineThreads = 256;
 constexpr int kCols = kCombineThreads * 4;  // columns per workgroup
 
+// Every expert row is read once and every output row written once, so both
+// bypass the caches' retention (non-temporal): at fine_prefill (537 MB of
+// rows) the combine went from 120 to 104 us alone, 63% to 73% of HBM.
+__device__ __forceinline__ f32x4 load_once(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_out(void* out, size_t at, const f32x4& acc) {
   if constexpr (OUT_BF16) {
-    uint2 pk;
-    pk.x = pack_bf16x2(acc[0], acc[1]);
-    pk.y = pack_bf16x2(acc[2], acc[3]);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + at) = pk;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + at));
   } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + at) = acc;
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(static_cast<float*>(out) + at));
   }
 }
 
@@ -60,9 +66,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   for (int k = 0; k < KMAX; ++k) {
     v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (r[k] >= 0) {
-      v[k] = *reinterpret_cast<const f32x4*>(y_rows + size_t(r[k]) * D + d);
-      for (int p = 1; p < nsplit; ++p)
-        v[k] += *reinterpret_cast<const f32x4*>(y_rows + p * split_stride + size_t(r[k]) * D + d);
+      v[k] = load_once(y_rows + size_t(r[k]) * D + d);
+      for (int p = 1; p < nsplit; ++p) v[k] += load_once(y_rows + p * split_stride + size_t(r[k]) * D + d);
     }
   }
   // slot order; the partials of one slot were added first
@@ -92,9 +97,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel_any_k(
     const int r = slot_source(slot_row, topk_idx, n, size_t(t) * K + k);
     if (r < 0) continue;
     const float g = gate[size_t(t) * K + k];
-    f32x4 v = *reinterpret_cast<const f32x4*>(y_rows + size_t(r) * D + d);
-    for (int p = 1; p < nsplit; ++p)
-      v += *reinterpret_cast<const f32x4*>(y_rows + p * split_stride + size_t(r) * D + d);
+    f32x4 v = load_once(y_rows + size_t(r) * D + d);
+    for (int p = 1; p < nsplit; ++p) v += load_once(y_rows + p * split_stride + size_t(r) * D + d);
     acc[0] = fmaf(g, v[0], acc[0]);
     acc[1] = fmaf(g, v[1], acc[1]);
     acc[2] = fmaf(g, v[2], acc[2]);

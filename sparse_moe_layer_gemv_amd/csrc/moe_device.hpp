@@ -91,10 +91,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // 16 bytes per lane from buffer offset voff + soff into LDS at dst + 16 * lane.
 // The range check applies to voff: an offset that must read as zero goes there.
+// NT: non-temporal cache policy (data read once, not to be kept in the caches).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff,
                                       uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
-                                           voff, soff, 0, 0);
+                                           voff, soff, 0, NT ? 2 : 0);
 }
 
 // Butterfly sum over the 64 lanes of a wavefront; every lane gets the total.
