@@ -59,7 +59,8 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
 //   topk_idx  int32 [T*K]     topk_gate fp32 [T*K]
 //   count     int32 [n]       offset    int32 [n+1]
 //   row_slot  int32 [cap]     slot_row  int32 [T*K]
-//   h         bf16  [cap][H]  y_rows    fp32  [2][cap][D] (split partials)
+//   h         bf16  [cap][H]  y_rows    fp32  [S][cap][D] (split partials: S = 2, or
+//                                           up to 4 on the weight-streaming path)
 // With the weight-streaming path the h region holds the fp32 first-product
 // results instead (decode_scratch_bytes).  The router's partial logits
 // (route_scratch_bytes) use the start of the y_rows region, which is written
@@ -68,7 +69,10 @@ struct Carve {
   size_t idx, gate, count, offset, row_slot, slot_row, h, y, total;
 };
 
-constexpr int kMaxSplits = 2;
+// Contraction partials of the second product the y_rows region holds.
+int y_planes(const Shape& s) {
+  return s.stream ? std::max(2, moe::decode_down_splits(s)) : 2;
+}
 
 Carve carve(const Shape& s) {
   Carve c{};
@@ -84,7 +88,7 @@ Carve carve(const Shape& s) {
   if (s.stream) h_bytes = std::max(h_bytes, moe::decode_scratch_bytes(s));
   c.h = o;        o = align_up(o + h_bytes, kAlign);
   c.y = o;
-  o = align_up(o + std::max(size_t(kMaxSplits) * s.cap * s.D * 4, moe::route_scratch_bytes(s)),
+  o = align_up(o + std::max(size_t(y_planes(s)) * s.cap * s.D * 4, moe::route_scratch_bytes(s)),
                kAlign);
   c.total = o;
   return c;
@@ -121,8 +125,8 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   *nsplit = 1;
   if (use_decode(s)) {
     *nsplit = y_part ? moe::decode_down_splits(s) : 1;
-    e = moe::launch_decode_down(s, count, offset, row_slot, topk_idx, ab, w2b, y_rows, *nsplit,
-                                y_part - y_rows, st);
+    e = moe::launch_decode_down(s, count, offset, row_slot, topk_idx, ab, w2b, y_rows, y_part,
+                                *nsplit, size_t(s.cap) * s.D, st);
   } else {
     *nsplit = y_part ? moe::grouped_down_splits(s) : 1;
     e = moe::launch_grouped_down(s, count, offset, h, w2b, y_rows, *nsplit, y_part - y_rows, st);
@@ -225,7 +229,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_
   st = run_ffn(s, x, expert_count, expert_offset, row_slot, nullptr, w1, w3, w2, y_rows, y_part,
                &nsplit, reinterpret_cast<uint16_t*>(base + c.h), hs);
   if (st != MOE_OK || nsplit == 1) return st;
-  return hip_status(moe::launch_add_rows(s, expert_offset, y_rows, y_part, hs));
+  return hip_status(moe::launch_add_rows(s, expert_offset, y_rows, y_part, nsplit - 1,
+                                         size_t(s.cap) * s.D, hs));
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int32_t* slot_row,

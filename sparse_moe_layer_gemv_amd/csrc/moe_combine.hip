@@ -140,22 +140,25 @@ hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_
                                             topk_gate, out, stream);
 }
 
+// Partials added in order, as the combine adds them: (y + p1) + p2 + ...
 __global__ __launch_bounds__(kCombineThreads) void add_rows_kernel(
     const int32_t* __restrict__ expert_offset, int n, int D, float* __restrict__ y,
-    const float* __restrict__ y_part) {
+    const float* __restrict__ y_part, int nparts, size_t part_stride) {
   const size_t total = size_t(expert_offset[n]) * D / 4;
   for (size_t i = size_t(blockIdx.x) * kCombineThreads + threadIdx.x; i < total;
        i += size_t(gridDim.x) * kCombineThreads) {
     f32x4 a = reinterpret_cast<f32x4*>(y)[i];
-    a += reinterpret_cast<const f32x4*>(y_part)[i];
+    for (int p = 0; p < nparts; ++p)
+      a += reinterpret_cast<const f32x4*>(y_part + p * part_stride)[i];
     reinterpret_cast<f32x4*>(y)[i] = a;
   }
 }
 
 hipError_t launch_add_rows(const Shape& s, const int32_t* expert_offset, float* y_rows,
-                           const float* y_part, hipStream_t stream) {
+                           const float* y_part, int nparts, size_t part_stride,
+                           hipStream_t stream) {
   hipLaunchKernelGGL(add_rows_kernel, dim3(1024), dim3(kCombineThreads), 0, stream, expert_offset,
-                     s.n, s.D, y_rows, y_part);
+                     s.n, s.D, y_rows, y_part, nparts, part_stride);
   return hipGetLastError();
 }
 

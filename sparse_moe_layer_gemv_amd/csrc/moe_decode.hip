@@ -9,8 +9,14 @@
 // exactly that read, once, coalesced, with many loads in flight, and use the
 // matrix cores only to keep the arithmetic off the critical path.
 //
-// Work split: a workgroup owns (expert e, 128 output columns, one weight
-// matrix); its waves split the contraction axis.  Per 32-wide step a lane
+// Work split: a workgroup owns (expert e, NB blocks of 128 output columns,
+// one weight matrix, one contraction range); its waves form NB groups, group g
+// taking block g, and a group's waves split the range.  With NB = 2 a
+// workgroup reads 512 contiguous bytes of every weight row at once (two waves
+// side by side), which streams faster than 256 in a load-only probe with
+// non-temporal loads (7.0 against 6.65 TB/s).  NB and the contraction splits
+// are chosen per shape (up_blocks, decode_up_splits, down_blocks,
+// decode_down_splits).  Per 32-wide step a lane
 // loads an 8 x 8 bf16 block of the matrix (8 rows x 16 bytes; 16 lanes cover
 // 256 contiguous bytes of a row), transposes it in registers, and feeds 8
 // v_mfma_f32_16x16x32_bf16 whose A rows are 16 output columns strided by 8
@@ -41,10 +47,20 @@ constexpr int kUpWaves = 8;
 constexpr int kDownWaves = 16;
 
 // 8 consecutive h values of one token-slot: bf16(silu(a) * b) from the fp32
-// first-product results.
-__device__ __forceinline__ uint4 h_fragment(const float* a, const float* b) {
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(a), a1 = *reinterpret_cast<const f32x4*>(a + 4);
-  const f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 4);
+// first-product results, which come as `nparts` contraction partials
+// `part_stride` floats apart and are added in order.
+__device__ __forceinline__ uint4 h_fragment(const float* a, const float* b, int nparts,
+                                            size_t part_stride) {
+  f32x4 a0 = *reinterpret_cast<const f32x4*>(a), a1 = *reinterpret_cast<const f32x4*>(a + 4);
+  f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 4);
+  for (int u = 1; u < nparts; ++u) {
+    const float* au = a + u * part_stride;
+    const float* bu = b + u * part_stride;
+    a0 += *reinterpret_cast<const f32x4*>(au);
+    a1 += *reinterpret_cast<const f32x4*>(au + 4);
+    b0 += *reinterpret_cast<const f32x4*>(bu);
+    b1 += *reinterpret_cast<const f32x4*>(bu + 4);
+  }
   return make_uint4(pack_bf16x2(silu(a0[0]) * b0[0], silu(a0[1]) * b0[1]),
                     pack_bf16x2(silu(a0[2]) * b0[2], silu(a0[3]) * b0[3]),
                     pack_bf16x2(silu(a1[0]) * b1[0], silu(a1[1]) * b1[1]),
@@ -52,34 +68,41 @@ __device__ __forceinline__ uint4 h_fragment(const float* a, const float* b) {
 }
 
 // UP:   x [T][Kdim] bf16 rows gathered through row_slot; w = w1 or w3 (by
-//       workgroup); out = ab fp32 [2][P][Ndim] (a at [0], b at [1], row = slot)
-// DOWN: ab rows through row_slot -> h; w = w2; out = y fp32 [cap][Ndim] + ks *
-//       split_stride (partial ks over contraction rows [ks*klen, +klen))
+//       workgroup); out = ab fp32 [nsplit][2][P][Ndim] (contraction partial
+//       ks; a at [ks][0], b at [ks][1], row = slot)
+// DOWN: ab rows (ab_parts partials) through row_slot -> h; w = w2; partial ks
+//       of y fp32 [cap][Ndim] at out (ks = 0) or y_part + (ks-1) * split_stride
+// Both: partial ks covers contraction rows [ks*klen, +klen).
 //
 // SCAN: the expert's token-slots are found by scanning the routing itself
 // (topk_idx, P = T*K entries, in slot order, so in the order the permute
 // would give them), and the second product writes its rows at the slot index
 // instead of the permuted row: no permute pass is needed.  Otherwise they come
 // from the permuted layout (expert_count, expert_offset, row_slot).
-template <bool UP, int RG, int WAVES, bool SCAN>
+template <bool UP, int RG, int WAVES, int NB, bool SCAN>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ ab,
     const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
     const int32_t* __restrict__ row_slot, const int32_t* __restrict__ topk_idx,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
-    int Kdim, int Ndim, int topk, int P, int ncb, int nsplit, int klen, ptrdiff_t split_stride) {
+    float* __restrict__ y_part, int Kdim, int Ndim, int topk, int P, int ncb, int nsplit,
+    int klen, size_t split_stride, int ab_parts) {
   constexpr int NACC = RG * 8;                     // f32x4 accumulators per lane
-  constexpr int RED_SLOTS = WAVES / 2;
-  __shared__ float red[RED_SLOTS * NACC * 4 * 64];
+  constexpr int WPG = WAVES / NB;                  // waves per column-block group
+  static_assert(WAVES % NB == 0 && (WPG & (WPG - 1)) == 0, "groups of a power of two");
+  __shared__ float red[(WAVES / 2) * NACC * 4 * 64];
 
-  // workgroup -> (expert, column block, matrix or contraction split)
-  const int per_e = ncb * (UP ? 2 : nsplit);
+  // workgroup -> (expert, column-block group, matrix (UP), contraction split)
+  const int groups = (ncb + NB - 1) / NB;
+  const int per_e = groups * (UP ? 2 : 1) * nsplit;
   const int e = blockIdx.x / per_e;
   const int r = blockIdx.x - e * per_e;
-  const int sub = UP ? (r & 1) : (r % nsplit);     // UP: matrix; DOWN: split
-  const int cb = UP ? (r >> 1) : (r / nsplit);
+  const int ks = r % nsplit;
+  const int mat = UP ? (r / nsplit) & 1 : 0;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int grp = wave / WPG, wl = wave - grp * WPG;
+  const int cb = (r / (nsplit * (UP ? 2 : 1))) * NB + grp;
   // SCAN: the expert's slots; every token holds an expert at most once, so
   // there are at most T <= 64 of them
   __shared__ int s_list[kStreamMaxTokens];
@@ -108,9 +131,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   const int n0 = cb * 128;
   const int kg = lane >> 4;
   const int nbk = lane & 15;
-  const bool col_ok = n0 + nbk * 8 < Ndim;
-  const int kbeg = UP ? 0 : sub * klen;
-  const int kend = UP ? Kdim : min(Kdim, kbeg + klen);
+  const bool col_ok = cb < ncb && n0 + nbk * 8 < Ndim;
+  const int kbeg = ks * klen;
+  const int kend = min(Kdim, kbeg + klen);
+  const size_t ab_stride = size_t(2) * P * Kdim;   // DOWN: floats between ab partials
 
   // activation row pointers (token row j = lane % 16 + 16 g of the expert)
   const uint16_t* xrow[RG];
@@ -140,7 +164,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     }
   }
   const uint16_t* wp =
-      (UP && sub ? w1 : w0) + size_t(e) * Kdim * Ndim + n0 + nbk * 8;
+      (UP && mat ? w1 : w0) + size_t(e) * Kdim * Ndim + (cb < ncb ? n0 : 0) + nbk * 8;
 
   f32x4 acc[RG][8];
 #pragma unroll
@@ -149,8 +173,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     for (int c = 0; c < 8; ++c) acc[g][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int steps = (kend - kbeg + 31) / 32;
-  const int per = (steps + WAVES - 1) / WAVES;
-  const int s0 = wave * per;
+  const int per = (steps + WPG - 1) / WPG;
+  const int s0 = wl * per;
   const int s1 = min(steps, s0 + per);
   for (int s = s0; s < s1; ++s) {
     const int kk = kbeg + s * 32 + kg * 8;
@@ -167,7 +191,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
         if (UP)
           v = *reinterpret_cast<const uint4*>(xrow[g] + kk);
         else
-          v = h_fragment(arow[g] + kk, brow[g] + kk);
+          v = h_fragment(arow[g] + kk, brow[g] + kk, ab_parts, ab_stride);
       }
       xv[g] = as_bf16x8(v);
     }
@@ -180,12 +204,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
         acc[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op[c]), xv[g], acc[g][c], 0, 0, 0);
   }
 
-  // Tree reduction over waves: at each level the upper half stores, the lower
-  // half adds.  Layout [slot][value][lane] keeps every store/load bank-clean.
+  // Tree reduction over each group's waves: at each level the upper half
+  // stores, the lower half adds.  Group g uses slots [g WPG/2, (g+1) WPG/2).
+  // Layout [slot][value][lane] keeps every store/load bank-clean.
 #pragma unroll
-  for (int half = WAVES / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half) {
-      float* dst = red + size_t(wave - half) * NACC * 4 * 64;
+  for (int half = WPG / 2; half >= 1; half >>= 1) {
+    if (wl >= half && wl < 2 * half) {
+      float* dst = red + size_t(grp * (WPG / 2) + wl - half) * NACC * 4 * 64;
       int v = 0;
 #pragma unroll
       for (int g = 0; g < RG; ++g)
@@ -195,8 +220,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
           for (int q = 0; q < 4; ++q, ++v) dst[v * 64 + lane] = acc[g][c][q];
     }
     __syncthreads();
-    if (wave < half) {
-      const float* src = red + size_t(wave) * NACC * 4 * 64;
+    if (wl < half) {
+      const float* src = red + size_t(grp * (WPG / 2) + wl) * NACC * 4 * 64;
       int v = 0;
 #pragma unroll
       for (int g = 0; g < RG; ++g)
@@ -207,7 +232,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     }
     __syncthreads();
   }
-  if (wave != 0) return;
+  if (wl != 0 || cb >= ncb) return;
 
   // Lane holds token row (lane & 15) + 16 g and, for register q, the 8
   // consecutive output columns n0 + (4 (lane >> 4) + q) * 8 + c, c = 0..7.
@@ -215,9 +240,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   for (int g = 0; g < RG; ++g) {
     if (!aval[g]) continue;
     const int j = (lane & 15) + 16 * g;
-    const size_t orow = UP ? size_t(sub) * P + slot_of[g]
+    const size_t orow = UP ? size_t(ks * 2 + mat) * P + slot_of[g]
                            : (SCAN ? size_t(slot_of[g]) : size_t(rbase + j));
-    float* op = static_cast<float*>(out) + (UP ? 0 : sub * split_stride) + orow * Ndim;
+    float* plane = UP || ks == 0 ? static_cast<float*>(out) : y_part + (ks - 1) * split_stride;
+    float* op = plane + orow * Ndim;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int col = n0 + (4 * (lane >> 4) + q) * 8;
@@ -230,50 +256,102 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   }
 }
 
-template <bool UP, int RG, int WAVES>
+template <bool UP, int RG, int WAVES, int NB>
 void launch_decode_rg(const Shape& s, dim3 grid, const uint16_t* x, const float* ab,
                       const int32_t* cnt, const int32_t* off, const int32_t* row_slot,
                       const int32_t* topk_idx, const uint16_t* w0, const uint16_t* w1, void* out,
-                      int Kdim, int Ndim, int P, int ncb, int nsplit, int klen,
-                      ptrdiff_t split_stride, hipStream_t stream) {
-  auto kern = topk_idx ? decode_kernel<UP, RG, WAVES, true> : decode_kernel<UP, RG, WAVES, false>;
+                      float* y_part, int Kdim, int Ndim, int P, int ncb, int nsplit, int klen,
+                      size_t split_stride, int ab_parts, hipStream_t stream) {
+  auto kern = topk_idx ? decode_kernel<UP, RG, WAVES, NB, true>
+                       : decode_kernel<UP, RG, WAVES, NB, false>;
   hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), 0, stream, x, ab, cnt, off, row_slot, topk_idx,
-                     w0, w1, out, Kdim, Ndim, s.K, P, ncb, nsplit, klen, split_stride);
+                     w0, w1, out, y_part, Kdim, Ndim, s.K, P, ncb, nsplit, klen, split_stride,
+                     ab_parts);
 }
 
-template <bool UP, int WAVES>
-hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const float* ab, const int32_t* cnt,
-                           const int32_t* off, const int32_t* row_slot, const int32_t* topk_idx,
-                           const uint16_t* w0, const uint16_t* w1, void* out, int Kdim, int Ndim,
-                           int nsplit, ptrdiff_t split_stride, hipStream_t stream) {
+// Column blocks per workgroup and contraction splits, by measurement (decode,
+// T = 16; first product + second product):
+//  - wide experts (H = 14336, 112 column blocks per matrix): two blocks per
+//    workgroup and no split in the first product (896 workgroups, 512 bytes of
+//    each weight row at once), two blocks in the second: 293 + 149 us, against
+//    295 + 154 with one block each, and 294-297 + 157 with the first product
+//    split in two (the second then adds two partials of a and b);
+//  - narrow experts (H = 768, 6 blocks): one block and the first product's
+//    contraction split in two (more workgroups): 175 + 97 us, against 183 + 96
+//    unsplit and 201 + 92 with two blocks unsplit.
+int up_blocks(const Shape& s) { return (s.H + 127) / 128 >= 32 ? 2 : 1; }
+
+template <bool UP, int WAVES, int NB>
+hipError_t launch_decode_nb(const Shape& s, const uint16_t* x, const float* ab,
+                            const int32_t* cnt, const int32_t* off, const int32_t* row_slot,
+                            const int32_t* topk_idx, const uint16_t* w0, const uint16_t* w1,
+                            void* out, float* y_part, int Kdim, int Ndim, int nsplit,
+                            size_t split_stride, int ab_parts, hipStream_t stream) {
   const int ncb = (Ndim + 127) / 128;
-  const dim3 grid(s.n * ncb * (UP ? 2 : nsplit));
+  const int groups = (ncb + NB - 1) / NB;
+  const dim3 grid(s.n * groups * (UP ? 2 : 1) * nsplit);
   const int P = s.T * s.K;
   const int klen = (Kdim + nsplit - 1) / nsplit;
   // more token rows per lane means more accumulators: fewer waves, so the
   // registers fit without spilling
   static_assert(kStreamMaxTokens <= 4 * kDecodeRows, "four row groups per lane at most");
   if (s.T <= kDecodeRows)
-    launch_decode_rg<UP, 1, WAVES>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
-                                   Kdim, Ndim, P, ncb, nsplit, klen, split_stride, stream);
+    launch_decode_rg<UP, 1, WAVES, NB>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                       y_part, Kdim, Ndim, P, ncb, nsplit, klen, split_stride,
+                                       ab_parts, stream);
   else if (s.T <= 2 * kDecodeRows)
-    launch_decode_rg<UP, 2, WAVES / 2>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
-                                       Kdim, Ndim, P, ncb, nsplit, klen, split_stride, stream);
+    launch_decode_rg<UP, 2, WAVES / 2, NB>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1,
+                                           out, y_part, Kdim, Ndim, P, ncb, nsplit, klen,
+                                           split_stride, ab_parts, stream);
   else
-    launch_decode_rg<UP, 4, WAVES / 2>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
-                                       Kdim, Ndim, P, ncb, nsplit, klen, split_stride, stream);
+    launch_decode_rg<UP, 4, WAVES / 2, NB>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1,
+                                           out, y_part, Kdim, Ndim, P, ncb, nsplit, klen,
+                                           split_stride, ab_parts, stream);
   return hipGetLastError();
+}
+
+template <bool UP, int WAVES>
+hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const float* ab, const int32_t* cnt,
+                           const int32_t* off, const int32_t* row_slot, const int32_t* topk_idx,
+                           const uint16_t* w0, const uint16_t* w1, void* out, float* y_part,
+                           int Kdim, int Ndim, int nsplit, size_t split_stride, int ab_parts,
+                           int nb, hipStream_t stream) {
+  if (nb == 2)
+    return launch_decode_nb<UP, WAVES, 2>(s, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                          y_part, Kdim, Ndim, nsplit, split_stride, ab_parts,
+                                          stream);
+  return launch_decode_nb<UP, WAVES, 1>(s, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                        y_part, Kdim, Ndim, nsplit, split_stride, ab_parts,
+                                        stream);
+}
+
+// Contraction splits of the first product (narrow experts only), while each
+// wave still gets at least 4 of the 32-deep steps.
+int decode_up_splits(const Shape& s) {
+  return up_blocks(s) == 1 && s.D % 64 == 0 && s.D / 2 >= 32 * 4 * kUpWaves ? 2 : 1;
+}
+
+// Two column blocks per workgroup in the second product when it reads a
+// single partial of a and b.
+int down_blocks(const Shape& s) {
+  return decode_up_splits(s) == 1 && (s.D + 127) / 128 >= 2 ? 2 : 1;
 }
 
 }  // namespace
 
 size_t decode_scratch_bytes(const Shape& s) {
-  return size_t(2) * s.T * s.K * s.H * 4;
+  return size_t(decode_up_splits(s)) * 2 * s.T * s.K * s.H * 4;
 }
 
 int decode_down_splits(const Shape& s) {
-  // split the contraction when each half still gives every wave whole steps
-  return (s.H % 64 == 0 && s.H / 2 >= 32 * kDownWaves) ? 2 : 1;
+  // Split the contraction while each part still gives every wave of a group at
+  // least 4 of the 32-deep steps; with two column blocks per workgroup, twice
+  // as many parts keep the workgroup count.
+  const int wpg = down_blocks(s) == 2 ? kDownWaves / 2 : kDownWaves;
+  int n = 1;
+  const int want = down_blocks(s) == 2 ? 4 : 2;
+  while (n < want && s.H % (64 * n) == 0 && s.H / (2 * n) >= 32 * 4 * wpg) n *= 2;
+  return n;
 }
 
 hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
@@ -281,29 +359,32 @@ hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* ex
                             const int32_t* topk_idx, const uint16_t* w1, const uint16_t* w3,
                             float* ab, hipStream_t stream) {
   return launch_decode_t<true, kUpWaves>(s, x, nullptr, expert_count, expert_offset, row_slot,
-                                         topk_idx, w1, w3, ab, s.D, s.H, 1, 0, stream);
+                                         topk_idx, w1, w3, ab, nullptr, s.D, s.H,
+                                         decode_up_splits(s), 0, 1, up_blocks(s), stream);
 }
 
 hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
                               const int32_t* expert_offset, const int32_t* row_slot,
                               const int32_t* topk_idx, const float* ab, const uint16_t* w2,
-                              float* y_rows, int nsplit, ptrdiff_t split_stride,
+                              float* y_rows, float* y_part, int nsplit, size_t part_stride,
                               hipStream_t stream) {
   // the most waves (up to kDownWaves) that still give each at least 4 of the
   // 32-deep steps: a short contraction (small experts) over 16 waves would
   // spend its time in the reduction
+  const int ab_parts = decode_up_splits(s);
   const int steps = (s.H + nsplit - 1) / nsplit / 32;
-  if (steps >= 4 * kDownWaves)
+  const int nb = down_blocks(s);
+  if (steps >= 4 * kDownWaves / nb)
     return launch_decode_t<false, kDownWaves>(s, nullptr, ab, expert_count, expert_offset,
-                                              row_slot, topk_idx, w2, nullptr, y_rows, s.H, s.D,
-                                              nsplit, split_stride, stream);
-  if (steps >= 4 * 8)
+                                              row_slot, topk_idx, w2, nullptr, y_rows, y_part,
+                                              s.H, s.D, nsplit, part_stride, ab_parts, nb, stream);
+  if (steps >= 4 * 8 / nb)
     return launch_decode_t<false, 8>(s, nullptr, ab, expert_count, expert_offset, row_slot,
-                                     topk_idx, w2, nullptr, y_rows, s.H, s.D, nsplit,
-                                     split_stride, stream);
+                                     topk_idx, w2, nullptr, y_rows, y_part, s.H, s.D, nsplit,
+                                     part_stride, ab_parts, nb, stream);
   return launch_decode_t<false, 4>(s, nullptr, ab, expert_count, expert_offset, row_slot,
-                                   topk_idx, w2, nullptr, y_rows, s.H, s.D, nsplit, split_stride,
-                                   stream);
+                                   topk_idx, w2, nullptr, y_rows, y_part, s.H, s.D, nsplit,
+                                   part_stride, ab_parts, nb, stream);
 }
 
 }  // namespace moe

@@ -58,9 +58,10 @@ hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
 
 // Weight-streaming path for small T (every touched expert's weights read once).
 // The first product writes fp32 a = x w1 and b = x w3 per token-slot into
-// `ab` ([2][T*K][H], decode_scratch_bytes); the second forms h = silu(a) * b
-// on the fly and may split its contraction into `nsplit` partial sums
-// (decode_down_splits), partial ks at y_rows + ks * split_stride.
+// `ab` ([S][2][T*K][H], S contraction partials; decode_scratch_bytes); the
+// second adds the partials, forms h = silu(a) * b on the fly and may split its
+// contraction into `nsplit` partial sums (decode_down_splits, at most 4):
+// partial 0 at y_rows, partial ks >= 1 at y_part + (ks-1) * part_stride.
 // Each expert's token-slots come from the permuted layout (expert_count,
 // expert_offset, row_slot; y rows at the permuted row) or, when topk_idx is
 // given, from scanning the routing (the others may be null; y rows at the
@@ -74,7 +75,7 @@ hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* ex
 hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
                               const int32_t* expert_offset, const int32_t* row_slot,
                               const int32_t* topk_idx, const float* ab, const uint16_t* w2,
-                              float* y_rows, int nsplit, ptrdiff_t split_stride,
+                              float* y_rows, float* y_part, int nsplit, size_t part_stride,
                               hipStream_t stream);
 
 // out[t] = sum_k gate[t][k] * (sum_p y_rows[p * split_stride + row(t,k)]),
@@ -89,8 +90,10 @@ hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_
 hipError_t launch_route_stats(const Shape& s, const int32_t* topk_idx, int32_t* counts,
                               hipStream_t stream);
 
-// y_rows[r] += y_part[r] for the rows of the expert segments (r < offset[n]).
+// y_rows[r] += y_part[p * part_stride + r] for p = 0 .. nparts-1 in order, for
+// the rows of the expert segments (r < offset[n]).
 hipError_t launch_add_rows(const Shape& s, const int32_t* expert_offset, float* y_rows,
-                           const float* y_part, hipStream_t stream);
+                           const float* y_part, int nparts, size_t part_stride,
+                           hipStream_t stream);
 
 }  // namespace moe
