@@ -84,6 +84,12 @@ SHAPES = [
     # split second product over more than one round of tiles, the last round
     # partly filled
     ("split_rounds", 2200, 2048, 1024, 8, 2, 38),
+    # weight streaming with two column blocks per workgroup and the second
+    # product's contraction in 4 partials (wide experts)
+    ("stream_wide_split4", 16, 512, 4096, 8, 2, 39),
+    # weight streaming with the first product's contraction in 2 partials
+    # (narrow experts), added before silu * mul
+    ("stream_narrow_up_split", 16, 2048, 256, 8, 2, 40),
 ]
 
 
@@ -340,8 +346,10 @@ def test_forward_graph_capture_replays_match_eager(moe, T, D, H, n, K):
 
 
 @pytest.mark.parametrize("T,D,H,n,K", [(300, 256, 1024, 8, 2), (16, 512, 1024, 8, 2),
-                                       (200, 256, 256, 160, 8)],
-                         ids=["tiled_split", "streaming_split", "n160"])
+                                       (200, 256, 256, 160, 8), (16, 512, 4096, 8, 2),
+                                       (16, 2048, 256, 8, 2)],
+                         ids=["tiled_split", "streaming_split", "n160", "streaming_split4",
+                              "streaming_up_split"])
 def test_stage_chain_matches_forward(moe, T, D, H, n, K):
     # moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine gives moe_forward's
     # output bit for bit (the stage path adds the split partials before the
