@@ -62,7 +62,10 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,      /* bad argument: null/misaligned pointer, bad size */
-  MOE_ENOTSUP = 2,     /* valid but unsupported shape (e.g. n_experts > 256) */
+  MOE_ENOTSUP = 2,     /* valid but unsupported shape: n_experts > 256, or a
+                        * size past the 32-bit offsets the kernels use
+                        * (D*H*2, T*D*2 or MOE_TILE_M*H*2 bytes >= 2^31, or
+                        * moe_capacity_rows >= 2^31) */
   MOE_EWORKSPACE = 3,  /* workspace missing or smaller than moe_workspace_bytes */
   MOE_EHIP = 4         /* a HIP launch failed */
 } moe_status_t;

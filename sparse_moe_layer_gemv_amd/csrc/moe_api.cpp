@@ -44,6 +44,7 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
   // of h with 32-bit byte offsets
   if (int64_t(p->dim) * p->hidden * 2 >= (int64_t(1) << 31)) return MOE_ENOTSUP;
   if (int64_t(p->tokens) * p->dim * 2 >= (int64_t(1) << 31)) return MOE_ENOTSUP;
+  if (int64_t(MOE_TILE_M) * p->hidden * 2 >= (int64_t(1) << 31)) return MOE_ENOTSUP;
   s->T = p->tokens;
   s->D = p->dim;
   s->H = p->hidden;

@@ -60,6 +60,12 @@ def test_capacity_and_workspace(moe):
     assert moe.workspace_bytes(moe.problem(16, 4100, 14336, 8, 2)) == 0    # dim % 8
     assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 257, 2)) == 0  # n > 256
     assert moe.workspace_bytes(moe.problem(16, 4096, 768, 256, 8)) > 0     # n = 256
+    # sizes past the kernels' 32-bit byte offsets are refused, the largest below them accepted
+    assert moe.workspace_bytes(moe.problem(262144, 4096, 64, 8, 2)) == 0    # T*D*2 = 2^31
+    assert moe.workspace_bytes(moe.problem(262143, 4096, 64, 8, 2)) > 0
+    assert moe.workspace_bytes(moe.problem(4, 16, 1 << 26, 8, 2)) == 0      # D*H*2 = 2^31
+    assert moe.workspace_bytes(moe.problem(4, 8, 1 << 22, 8, 2)) == 0       # 256*H*2 = 2^31
+    assert moe.workspace_bytes(moe.problem(4, 8, (1 << 22) - 8, 8, 2)) > 0
     assert moe.decode_max_tokens() >= 16
     # expert-product path: unknown values are invalid; forced streaming only up
     # to decode_max_tokens(); its scratch is part of the workspace
