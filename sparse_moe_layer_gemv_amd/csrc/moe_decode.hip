@@ -92,17 +92,21 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   static_assert(WAVES % NB == 0 && (WPG & (WPG - 1)) == 0, "groups of a power of two");
   __shared__ float red[(WAVES / 2) * NACC * 4 * 64];
 
-  // workgroup -> (expert, column-block group, matrix (UP), contraction split)
+  // workgroup -> (expert, matrix (UP), column-block group, contraction
+  // split), split fastest.  Matrix-major inside an expert (all of w1's
+  // column blocks, then w3's) streams faster than alternating w1 and w3
+  // between neighbouring workgroups.
   const int groups = (ncb + NB - 1) / NB;
-  const int per_e = groups * (UP ? 2 : 1) * nsplit;
+  const int per_mat = groups * nsplit;
+  const int per_e = per_mat * (UP ? 2 : 1);
   const int e = blockIdx.x / per_e;
   const int r = blockIdx.x - e * per_e;
   const int ks = r % nsplit;
-  const int mat = UP ? (r / nsplit) & 1 : 0;
+  const int mat = UP ? r / per_mat : 0;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int grp = wave / WPG, wl = wave - grp * WPG;
-  const int cb = (r / (nsplit * (UP ? 2 : 1))) * NB + grp;
+  const int cb = ((r - mat * per_mat) / nsplit) * NB + grp;
   // SCAN: the expert's slots; every token holds an expert at most once, so
   // there are at most T <= 64 of them
   __shared__ int s_list[kStreamMaxTokens];
