@@ -67,7 +67,9 @@ typedef enum {
                         * (D*H*2, T*D*2 or MOE_TILE_M*H*2 bytes >= 2^31, or
                         * moe_capacity_rows >= 2^31) */
   MOE_EWORKSPACE = 3,  /* workspace missing or smaller than moe_workspace_bytes */
-  MOE_EHIP = 4         /* a HIP launch failed */
+  MOE_EHIP = 4         /* a HIP launch failed: hipGetLastError() after the
+                        * launch was not hipSuccess (this also reports an
+                        * earlier error the calling thread had not read) */
 } moe_status_t;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;

@@ -130,7 +130,7 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
                                 *nsplit, size_t(s.cap) * s.D, st);
   } else {
     *nsplit = y_part ? moe::grouped_down_splits(s) : 1;
-    e = moe::launch_grouped_down(s, count, offset, h, w2b, y_rows, *nsplit, y_part - y_rows, st);
+    e = moe::launch_grouped_down(s, count, offset, h, w2b, y_rows, *nsplit, y_part, st);
   }
   if (e != hipSuccess || (mark && mark(4) != hipSuccess)) return MOE_EHIP;
   return MOE_OK;
@@ -226,7 +226,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_
   float* y_part = reinterpret_cast<float*>(base + c.y);
   int nsplit = 1;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // the split partial is written y_part - y_rows floats after y_rows
+  // a split second product leaves its partials beyond the first in the
+  // workspace; they are added into y_rows in order
   st = run_ffn(s, x, expert_count, expert_offset, row_slot, nullptr, w1, w3, w2, y_rows, y_part,
                &nsplit, reinterpret_cast<uint16_t*>(base + c.h), hs);
   if (st != MOE_OK || nsplit == 1) return st;

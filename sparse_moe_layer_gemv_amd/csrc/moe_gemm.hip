@@ -645,14 +645,14 @@ __device__ __forceinline__ void down_tile(const int32_t* __restrict__ expert_cou
   }
 }
 
-// The contraction (H) can be split into `nsplit` ranges of `klen` elements;
-// split ks writes its partial product to y + ks * split_stride, and the
-// partials are added (in split order) by the consumer.
+// The contraction (H) can be split into `nsplit` (1 or 2) ranges of `klen`
+// elements; range 0 writes its partial product to y and range 1 to y_part
+// (which may lie in another allocation), and the consumer adds the two.
 template <bool EVEN, bool WNT>
 __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
     const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2, float* __restrict__ y,
-    int D, int H, int n, int nsplit, int klen, ptrdiff_t split_stride) {
+    int D, int H, int n, int nsplit, int klen, float* __restrict__ y_part) {
   const int nt_count = (D + 2 * SUBN - 1) / (2 * SUBN);
   // persistent, as the first product: tiles L, L + G, ... of this XCD, the
   // next tile's mapping read while the current one runs
@@ -671,9 +671,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
     const int nt = unit - ks * nt_count;
     const int kbase = ks * klen;
     const int ksteps = (min(klen, H - kbase) + BK - 1) / BK;
-    // y + ks * split_stride may point into another allocation (the workspace)
-    down_tile<EVEN, WNT>(expert_count, expert_offset, h, w2, y + ks * split_stride, D, H, mt,
-                    nt * 2 * SUBN, e, kbase, ksteps);
+    down_tile<EVEN, WNT>(expert_count, expert_offset, h, w2, ks == 0 ? y : y_part, D, H, mt,
+                         nt * 2 * SUBN, e, kbase, ksteps);
     stage_barrier();  // every wave is past this tile's LDS use before the next tile's loads
     if (!more) return;
     L += gridDim.x;
@@ -685,20 +684,23 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
 
 
 // One workgroup per compute unit (a multiple of 8, so that tile L + G stays
-// on the XCD of tile L); read once per device.
-// Host threads may race here; they all store the same value.
+// on the XCD of tile L); read once per device (devices 0..63; any further
+// device is queried on every call).  Host threads may race here; they all
+// store the same value.
 int persistent_workgroups() {
-  static std::atomic<int> cached[64];
+  constexpr int kCachedDevices = 64;
+  static std::atomic<int> cached[kCachedDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int g = cached[dev].load(std::memory_order_relaxed);
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const bool cacheable = dev < kCachedDevices;
+  int g = cacheable ? cached[dev].load(std::memory_order_relaxed) : 0;
   if (g == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 8)
       cus = 256;
     g = cus / 8 * 8;
-    cached[dev].store(g, std::memory_order_relaxed);
+    if (cacheable) cached[dev].store(g, std::memory_order_relaxed);
   }
   return g;
 }
@@ -757,8 +759,9 @@ int grouped_down_splits(const Shape& s) {
 
 hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
                                const int32_t* expert_offset, const uint16_t* h,
-                               const uint16_t* w2, float* y_rows, int nsplit, ptrdiff_t split_stride,
+                               const uint16_t* w2, float* y_rows, int nsplit, float* y_part,
                                hipStream_t stream) {
+  if (nsplit < 1 || nsplit > 2 || (nsplit == 2 && !y_part)) return hipErrorInvalidValue;
   const int mt_max = int(s.cap / BM);
   const int nt = (s.D + 2 * SUBN - 1) / (2 * SUBN);
   if (mt_max * nt * nsplit == 0) return hipSuccess;
@@ -770,11 +773,14 @@ hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
   if (even) {
     auto kern = wnt ? grouped_down_kernel<true, true> : grouped_down_kernel<true, false>;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), 0, stream, expert_count, expert_offset, h,
-                       w2, y_rows, s.D, s.H, s.n, nsplit, klen, split_stride);
+                       w2, y_rows, s.D, s.H, s.n, nsplit, klen, y_part);
   } else {
+    // the ragged kernel runs the whole contraction: only one partial
+    // (grouped_down_splits never splits such shapes)
+    if (nsplit != 1) return hipErrorInvalidValue;
     auto kern = wnt ? grouped_down_kernel<false, true> : grouped_down_kernel<false, false>;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), 0, stream, expert_count, expert_offset, h,
-                       w2, y_rows, s.D, s.H, s.n, 1, s.H, split_stride);
+                       w2, y_rows, s.D, s.H, s.n, 1, s.H, y_part);
   }
   return hipGetLastError();
 }

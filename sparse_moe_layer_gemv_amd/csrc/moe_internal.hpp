@@ -46,14 +46,14 @@ hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* expe
 hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_offset,
                              const int32_t* row_slot, const uint16_t* w1, const uint16_t* w3,
                              uint16_t* h, hipStream_t stream);
-// The second product may be split along its contraction into `nsplit`
-// partial sums: partial ks at y_rows + ks * split_stride (see
-// grouped_down_splits).
+// The second product may be split along its contraction into nsplit = 2
+// partial sums (see grouped_down_splits): partial 0 at y_rows, partial 1 at
+// y_part (unused, may be null, when nsplit = 1).
 int grouped_down_splits(const Shape& s);
 // Rows past an expert's slots (padding) are not written.
 hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
                                const int32_t* expert_offset, const uint16_t* h,
-                               const uint16_t* w2, float* y_rows, int nsplit, ptrdiff_t split_stride,
+                               const uint16_t* w2, float* y_rows, int nsplit, float* y_part,
                                hipStream_t stream);
 
 // Weight-streaming path for small T (every touched expert's weights read once).
