@@ -32,10 +32,15 @@
  *    on `stream` (a hipStream_t; NULL is the default stream).  There is no
  *    device-to-host read and no synchronisation inside the library, so a call
  *    can be captured into a HIP graph.
- *  - Errors: arguments are checked before anything is enqueued; on error the
- *    function returns a non-zero moe_status_t and enqueues nothing.  A failed
- *    kernel launch returns MOE_EHIP.  tokens == 0 is a valid no-op.  No C++
+ *  - Errors: arguments are checked before anything is enqueued; on an
+ *    argument error the function returns a non-zero moe_status_t and enqueues
+ *    nothing.  A failed kernel launch returns MOE_EHIP (kernels enqueued
+ *    before it stay enqueued).  tokens == 0 is a valid no-op.  No C++
  *    exception crosses this interface.
+ *  - A workspace holds a call's intermediate results until that call's last
+ *    kernel has run, so calls that may run concurrently (on different
+ *    streams, or in parallel branches of one graph) need separate
+ *    workspaces.  Calls in order on one stream may share one.
  *  - Pointers must be 16-byte aligned; dim and hidden must be multiples of 8;
  *    1 <= top_k <= n_experts <= MOE_MAX_EXPERTS.
  *  - Ties in TopK go to the lower expert index; slot 0 of each token holds the

@@ -345,6 +345,37 @@ def test_forward_graph_capture_replays_match_eager(moe, T, D, H, n, K):
         assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {r}"
 
 
+def test_concurrent_streams_with_separate_workspaces(moe):
+    # Calls that may overlap need separate workspaces; with them, a tiled and a
+    # weight-streaming forward enqueued on two streams at once (each a few
+    # times, interleaved) give their one-stream results bit for bit.
+    import torch
+    layers = [moe_synth.make_layer(300, 256, 1024, 8, 2, seed=410),
+              moe_synth.make_layer(16, 512, 1024, 8, 2, seed=411)]
+    runs = []
+    for L in layers:
+        T, D, H, n, K = L.shape
+        d = _upload(L)
+        ws = torch.empty(moe.workspace_bytes(moe.problem(T, D, H, n, K)), dtype=torch.uint8,
+                         device="cuda:0")
+        args = (d["x"], d["wg"], d["w1"], d["w3"], d["w2"], K)
+        ref = host(moe.forward(*args, workspace=ws)).copy()
+        outs = [torch.full((T, D), float("nan"), device="cuda:0") for _ in range(3)]
+        runs.append((args, ws, ref, outs))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in runs]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for (args, ws, _, outs), s_ in zip(runs, streams):
+            with torch.cuda.stream(s_):
+                moe.forward(*args, out=outs[rep], workspace=ws)
+    torch.cuda.synchronize()
+    for i, (_, _, ref, outs) in enumerate(runs):
+        for rep, o in enumerate(outs):
+            assert np.array_equal(host(o).view(np.uint32), ref.view(np.uint32)), (i, rep)
+
+
 @pytest.mark.parametrize("T,D,H,n,K", [(300, 256, 1024, 8, 2), (16, 512, 1024, 8, 2),
                                        (200, 256, 256, 160, 8), (16, 512, 4096, 8, 2),
                                        (16, 2048, 256, 8, 2)],
