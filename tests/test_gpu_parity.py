@@ -90,6 +90,11 @@ SHAPES = [
     # weight streaming with the first product's contraction in 2 partials
     # (narrow experts), added before silu * mul
     ("stream_narrow_up_split", 16, 2048, 256, 8, 2, 40),
+    # the router's workgroup shape changes at 64 tokens (one token per
+    # workgroup up to 64, four above); 16 experts at a decode-size batch
+    ("router_t64", 64, 256, 384, 8, 2, 42),
+    ("router_t65", 65, 256, 384, 8, 2, 43),
+    ("decode_n16_k2", 24, 256, 384, 16, 2, 44),
 ]
 
 
