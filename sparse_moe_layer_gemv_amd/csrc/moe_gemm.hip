@@ -126,16 +126,24 @@ __device__ __forceinline__ bf16x8 lds_read_wfrag(uint8_t* base, uint32_t off) {
 // the 8 XCDs round-robin (workgroup L runs on XCD L % 8) and each XCD has its
 // own L2.  Valid workgroups (L < total tiles) are renumbered so that XCD x
 // gets a contiguous range v of a linear tile order, and that order walks the
-// experts one after the other; within an expert, column-tile by column-tile,
-// with all of the expert's row-tiles consecutive.  So the workgroups resident
-// on one XCD at a time work on one expert and share each weight panel (read
-// once into that L2) and a few activation panels.
+// experts one after the other; within an expert, row block by row block, and
+// within a block column-tile by column-tile with the block's row-tiles
+// consecutive.  So the workgroups resident on one XCD at a time work on one
+// expert and share each weight panel (read once into that L2) and a few
+// activation panels.  An expert with fewer than 2 kRowBlock row tiles is one
+// block; a larger one is cut into blocks of kRowBlock to 2 kRowBlock - 1 row
+// tiles.  One XCD runs 32 tiles at a time, and with all of a large expert's
+// row tiles side by side (32 of them for one expert of 8192 rows) its whole
+// activation panel was fetched again for every column tile; with blocks, each
+// weight panel is fetched once per block instead.
 //   offset: segment starts (tile-aligned), n experts, nu: column units per row
 //   tile.  Returns false for workgroups beyond the valid tiles.
 // Expert e's tiles are v in [nu*offset[e]/BM, nu*offset[e+1]/BM), so the
 // expert is the last e whose segment starts at or before v: a binary search
 // over the monotone offsets (empty experts share their start with the next
 // one, and the last of equal starts is the non-empty segment).
+constexpr int kRowBlock = 8;  // row tiles per block of the tile order
+
 __device__ __forceinline__ void decode_tile(int v, const int32_t* __restrict__ offset, int n,
                                             int nu, int& mt, int& unit, int& expert) {
   int lo = 0, hi = n - 1;  // invariant: the answer lies in [lo, hi]
@@ -146,8 +154,24 @@ __device__ __forceinline__ void decode_tile(int v, const int32_t* __restrict__ o
   const int m0 = offset[lo] / BM;
   const int me = offset[lo + 1] / BM - m0;
   const int vl = v - m0 * nu;
-  mt = m0 + vl % me;
-  unit = vl / me;
+  if (me < 2 * kRowBlock) {  // one block
+    mt = m0 + vl % me;
+    unit = vl / me;
+    expert = lo;
+    return;
+  }
+  // nb = me / kRowBlock blocks of q or q + 1 row tiles, the first r of them
+  // the larger; block b covers tiles [nu*start, nu*(start + size)) of the
+  // expert, so vl / nu locates it
+  const int nb = me / kRowBlock;
+  const int q = me / nb, r = me - q * nb;
+  const int rp = vl / nu;
+  const int b = rp < r * (q + 1) ? rp / (q + 1) : r + (rp - r * (q + 1)) / q;
+  const int start = b * q + min(b, r);
+  const int size = q + (b < r ? 1 : 0);
+  const int w = vl - nu * start;
+  mt = m0 + start + w % size;
+  unit = w / size;
   expert = lo;
 }
 

@@ -95,6 +95,9 @@ SHAPES = [
     ("router_t64", 64, 256, 384, 8, 2, 42),
     ("router_t65", 65, 256, 384, 8, 2, 43),
     ("decode_n16_k2", 24, 256, 384, 16, 2, 44),
+    # one expert with 12 row tiles: a full block of 8 row tiles in the tile
+    # order, then a partial block of 4
+    ("one_expert_12_row_tiles", 3000, 256, 512, 1, 1, 45),
 ]
 
 
