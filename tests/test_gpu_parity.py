@@ -95,9 +95,9 @@ SHAPES = [
     ("router_t64", 64, 256, 384, 8, 2, 42),
     ("router_t65", 65, 256, 384, 8, 2, 43),
     ("decode_n16_k2", 24, 256, 384, 16, 2, 44),
-    # one expert with 12 row tiles: a full block of 8 row tiles in the tile
-    # order, then a partial block of 4
-    ("one_expert_12_row_tiles", 3000, 256, 512, 1, 1, 45),
+    # one expert with 17 row tiles: cut into blocks of 9 and 8 row tiles in
+    # the tiled products' tile order (an expert is cut from 16 row tiles on)
+    ("one_expert_17_row_tiles", 4200, 256, 512, 1, 1, 45),
 ]
 
 
@@ -193,6 +193,9 @@ FORCED = [
     # H = 1024: the second product runs as two contraction halves whose
     # partial sums are added before returning y_rows
     ("split_contraction", lambda T: np.stack([np.arange(T) % 8, (np.arange(T) + 3) % 8], 1), 900, 512, 1024),
+    # two experts of 17 row tiles each: both cut into row blocks of 9 and 8 in
+    # the tile order
+    ("two_experts_17_row_tiles", lambda T: np.tile([[5, 2]], (T, 1)), 4200, 256, 384),
 ]
 
 
