@@ -139,7 +139,9 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate
  *   row_slot      int32 [cap]     out: slot held by each permuted row, -1 for
  *                                     padding (cap = moe_capacity_rows)
  *   slot_row      int32 [T*K]     out: permuted row of each slot (-1 if dropped)
- * Within an expert, slots keep increasing slot order (stable). */
+ * Within an expert, slots keep increasing slot order (stable).  A token may
+ * name an expert more than once (the router never does; a caller's routing
+ * may): each such slot is a row of its own. */
 moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx,
                          int32_t* expert_count, int32_t* expert_offset,
                          int32_t* row_slot, int32_t* slot_row, void* stream);
@@ -152,10 +154,13 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx,
  *   expert_count  int32 [n], expert_offset int32 [n+1], row_slot int32 [cap]
  *                                 in: as written by moe_permute
  *   w1, w3 bf16 [n][D][H], w2 bf16 [n][H][D]   in
- *   y_rows        fp32 [cap][D]   out (rows of padding are left as they were)
+ *   y_rows        fp32 [cap][D]   out: rows offset[e] .. offset[e]+count[e]-1
+ *                                 of every expert; rows of padding are left
+ *                                 as they were
  *   ws, ws_bytes  workspace, >= moe_workspace_bytes(p)
  * The intermediate silu(a)*b is rounded once to bf16 (it is the input of the
- * second product); products accumulate in fp32. */
+ * second product); products accumulate in fp32.  Every row of an expert is
+ * computed, whatever its count (up to T*K when tokens repeat an expert). */
 moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x,
                              const int32_t* expert_count, const int32_t* expert_offset,
                              const int32_t* row_slot, const void* w1, const void* w3,
@@ -217,6 +222,7 @@ moe_status_t moe_route_stats(const moe_problem_t* p, const int32_t* topk_idx, in
 /* Largest T for which moe_forward and moe_grouped_ffn take the weight-streaming
  * (decode) path. */
 int32_t moe_decode_max_tokens(void);
+
 
 #ifdef __cplusplus
 }

@@ -231,8 +231,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_
   st = run_ffn(s, x, expert_count, expert_offset, row_slot, nullptr, w1, w3, w2, y_rows, y_part,
                &nsplit, reinterpret_cast<uint16_t*>(base + c.h), hs);
   if (st != MOE_OK || nsplit == 1) return st;
-  return hip_status(moe::launch_add_rows(s, expert_offset, y_rows, y_part, nsplit - 1,
-                                         size_t(s.cap) * s.D, hs));
+  return hip_status(moe::launch_add_rows(s, expert_count, expert_offset, y_rows, y_part,
+                                         nsplit - 1, size_t(s.cap) * s.D, hs));
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int32_t* slot_row,

@@ -4,6 +4,8 @@
 // chosen experts contribute.  out[t] = sum_k gate[t][k] * y_rows[slot_row[t*K+k]],
 // summed in slot order k = 0, 1, ... (a gather, no atomics, so it is
 // deterministic).  Bound by HBM: reads K fp32 rows and writes one row per token.
+#include <algorithm>
+
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -141,24 +143,31 @@ hipError_t launch_combine(const Shape& s, const float* y_rows, int nsplit, size_
 }
 
 // Partials added in order, as the combine adds them: (y + p1) + p2 + ...
+// Only the rows that hold token-slots (offset[e] .. offset[e] + count[e] of
+// each expert) are touched; padding rows are left as they were.  Workgroups
+// (x, e) stride over expert e's rows (blockIdx.y = expert).
 __global__ __launch_bounds__(kCombineThreads) void add_rows_kernel(
-    const int32_t* __restrict__ expert_offset, int n, int D, float* __restrict__ y,
-    const float* __restrict__ y_part, int nparts, size_t part_stride) {
-  const size_t total = size_t(expert_offset[n]) * D / 4;
+    const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset, int D,
+    float* __restrict__ y, const float* __restrict__ y_part, int nparts, size_t part_stride) {
+  const int e = blockIdx.y;
+  const size_t first = size_t(expert_offset[e]) * D / 4;
+  const size_t total = size_t(expert_count[e]) * D / 4;
   for (size_t i = size_t(blockIdx.x) * kCombineThreads + threadIdx.x; i < total;
        i += size_t(gridDim.x) * kCombineThreads) {
-    f32x4 a = reinterpret_cast<f32x4*>(y)[i];
+    f32x4 a = reinterpret_cast<f32x4*>(y)[first + i];
     for (int p = 0; p < nparts; ++p)
-      a += reinterpret_cast<const f32x4*>(y_part + p * part_stride)[i];
-    reinterpret_cast<f32x4*>(y)[i] = a;
+      a += reinterpret_cast<const f32x4*>(y_part + p * part_stride)[first + i];
+    reinterpret_cast<f32x4*>(y)[first + i] = a;
   }
 }
 
-hipError_t launch_add_rows(const Shape& s, const int32_t* expert_offset, float* y_rows,
-                           const float* y_part, int nparts, size_t part_stride,
-                           hipStream_t stream) {
-  hipLaunchKernelGGL(add_rows_kernel, dim3(1024), dim3(kCombineThreads), 0, stream, expert_offset,
-                     s.n, s.D, y_rows, y_part, nparts, part_stride);
+hipError_t launch_add_rows(const Shape& s, const int32_t* expert_count,
+                           const int32_t* expert_offset, float* y_rows, const float* y_part,
+                           int nparts, size_t part_stride, hipStream_t stream) {
+  // about 1024 workgroups over all experts
+  const int per_expert = std::max(1, 1024 / s.n);
+  hipLaunchKernelGGL(add_rows_kernel, dim3(per_expert, s.n), dim3(kCombineThreads), 0, stream,
+                     expert_count, expert_offset, s.D, y_rows, y_part, nparts, part_stride);
   return hipGetLastError();
 }
 

@@ -139,123 +139,134 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   const int kbeg = ks * klen;
   const int kend = min(Kdim, kbeg + klen);
   const size_t ab_stride = size_t(2) * P * Kdim;   // DOWN: floats between ab partials
-
-  // activation row pointers (token row j = lane % 16 + 16 g of the expert)
-  const uint16_t* xrow[RG];
-  const float* arow[RG];
-  const float* brow[RG];
-  bool aval[RG];
-  int slot_of[RG];
-#pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    const int j = (lane & 15) + 16 * g;
-    aval[g] = j < cnt;
-    int slot = 0;
-    if (aval[g]) {
-      if constexpr (SCAN) {
-        slot = s_list[j];
-      } else {
-        slot = row_slot[rbase + j];
-      }
-    }
-    slot_of[g] = slot;
-    const int sl = slot >= 0 ? slot : 0;
-    if (UP) {
-      xrow[g] = x + size_t(sl / topk) * Kdim;
-    } else {
-      arow[g] = ab + size_t(sl) * Kdim;
-      brow[g] = ab + (size_t(P) + sl) * Kdim;
-    }
-  }
   const uint16_t* wp =
       (UP && mat ? w1 : w0) + size_t(e) * Kdim * Ndim + (cb < ncb ? n0 : 0) + nbk * 8;
-
-  f32x4 acc[RG][8];
-#pragma unroll
-  for (int g = 0; g < RG; ++g)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[g][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   const int steps = (kend - kbeg + 31) / 32;
   const int per = (steps + WPG - 1) / WPG;
   const int s0 = wl * per;
   const int s1 = min(steps, s0 + per);
-  for (int s = s0; s < s1; ++s) {
-    const int kk = kbeg + s * 32 + kg * 8;
-    const bool kok = kk < kend;
-    uint4 wv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      wv[j] = (kok && col_ok) ? load_weight(wp + size_t(kk + j) * Ndim) : make_uint4(0, 0, 0, 0);
-    bf16x8 xv[RG];
+
+  // Passes of 16 RG token rows.  RG is chosen from T, and an expert holds at
+  // most T rows when every token names it at most once (always so under
+  // moe_forward, whose router picks K distinct experts); a caller's layout
+  // for moe_grouped_ffn may name an expert twice for one token, and then the
+  // rows beyond the first pass take further passes over the weights.  cnt
+  // is uniform over the workgroup, so every wave runs the same passes (the
+  // reduction's barriers).
+  for (int jb = 0; jb < cnt; jb += 16 * RG) {
+    // activation row pointers (token row j = jb + lane % 16 + 16 g of the expert)
+    const uint16_t* xrow[RG];
+    const float* arow[RG];
+    const float* brow[RG];
+    bool aval[RG];
+    int slot_of[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kok && aval[g]) {
-        if (UP)
-          v = *reinterpret_cast<const uint4*>(xrow[g] + kk);
-        else
-          v = h_fragment(arow[g] + kk, brow[g] + kk, ab_parts, ab_stride);
+      const int j = jb + (lane & 15) + 16 * g;
+      aval[g] = j < cnt;
+      int slot = 0;
+      if (aval[g]) {
+        if constexpr (SCAN) {
+          slot = s_list[j];
+        } else {
+          slot = row_slot[rbase + j];
+        }
       }
-      xv[g] = as_bf16x8(v);
+      slot_of[g] = slot;
+      const int sl = slot >= 0 ? slot : 0;
+      if (UP) {
+        xrow[g] = x + size_t(sl / topk) * Kdim;
+      } else {
+        arow[g] = ab + size_t(sl) * Kdim;
+        brow[g] = ab + (size_t(P) + sl) * Kdim;
+      }
     }
-    uint4 op[8];
-    transpose8x8_bf16(wv, op);
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int g = 0; g < RG; ++g)
-        acc[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op[c]), xv[g], acc[g][c], 0, 0, 0);
-  }
 
-  // Tree reduction over each group's waves: at each level the upper half
-  // stores, the lower half adds.  Group g uses slots [g WPG/2, (g+1) WPG/2).
-  // Layout [slot][value][lane] keeps every store/load bank-clean.
+    f32x4 acc[RG][8];
 #pragma unroll
-  for (int half = WPG / 2; half >= 1; half >>= 1) {
-    if (wl >= half && wl < 2 * half) {
-      float* dst = red + size_t(grp * (WPG / 2) + wl - half) * NACC * 4 * 64;
-      int v = 0;
+    for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int g = 0; g < RG; ++g)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int q = 0; q < 4; ++q, ++v) dst[v * 64 + lane] = acc[g][c][q];
-    }
-    __syncthreads();
-    if (wl < half) {
-      const float* src = red + size_t(grp * (WPG / 2) + wl) * NACC * 4 * 64;
-      int v = 0;
-#pragma unroll
-      for (int g = 0; g < RG; ++g)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int q = 0; q < 4; ++q, ++v) acc[g][c][q] += src[v * 64 + lane];
-    }
-    __syncthreads();
-  }
-  if (wl != 0 || cb >= ncb) return;
+      for (int c = 0; c < 8; ++c) acc[g][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Lane holds token row (lane & 15) + 16 g and, for register q, the 8
-  // consecutive output columns n0 + (4 (lane >> 4) + q) * 8 + c, c = 0..7.
+    for (int s = s0; s < s1; ++s) {
+      const int kk = kbeg + s * 32 + kg * 8;
+      const bool kok = kk < kend;
+      uint4 wv[8];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    if (!aval[g]) continue;
-    const int j = (lane & 15) + 16 * g;
-    const size_t orow = UP ? size_t(ks * 2 + mat) * P + slot_of[g]
-                           : (SCAN ? size_t(slot_of[g]) : size_t(rbase + j));
-    float* plane = UP || ks == 0 ? static_cast<float*>(out) : y_part + (ks - 1) * split_stride;
-    float* op = plane + orow * Ndim;
+      for (int j = 0; j < 8; ++j)
+        wv[j] = (kok && col_ok) ? load_weight(wp + size_t(kk + j) * Ndim) : make_uint4(0, 0, 0, 0);
+      bf16x8 xv[RG];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = n0 + (4 * (lane >> 4) + q) * 8;
-      if (col >= Ndim) continue;
-      *reinterpret_cast<f32x4*>(op + col) =
-          f32x4{acc[g][0][q], acc[g][1][q], acc[g][2][q], acc[g][3][q]};
-      *reinterpret_cast<f32x4*>(op + col + 4) =
-          f32x4{acc[g][4][q], acc[g][5][q], acc[g][6][q], acc[g][7][q]};
+      for (int g = 0; g < RG; ++g) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (kok && aval[g]) {
+          if (UP)
+            v = *reinterpret_cast<const uint4*>(xrow[g] + kk);
+          else
+            v = h_fragment(arow[g] + kk, brow[g] + kk, ab_parts, ab_stride);
+        }
+        xv[g] = as_bf16x8(v);
+      }
+      uint4 op[8];
+      transpose8x8_bf16(wv, op);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+          acc[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op[c]), xv[g], acc[g][c], 0, 0, 0);
+    }
+
+    // Tree reduction over each group's waves: at each level the upper half
+    // stores, the lower half adds.  Group g uses slots [g WPG/2, (g+1) WPG/2).
+    // Layout [slot][value][lane] keeps every store/load bank-clean.  The
+    // barrier closing each level also orders this pass's last reads of `red`
+    // before the next pass's first stores.
+#pragma unroll
+    for (int half = WPG / 2; half >= 1; half >>= 1) {
+      if (wl >= half && wl < 2 * half) {
+        float* dst = red + size_t(grp * (WPG / 2) + wl - half) * NACC * 4 * 64;
+        int v = 0;
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q, ++v) dst[v * 64 + lane] = acc[g][c][q];
+      }
+      __syncthreads();
+      if (wl < half) {
+        const float* src = red + size_t(grp * (WPG / 2) + wl) * NACC * 4 * 64;
+        int v = 0;
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q, ++v) acc[g][c][q] += src[v * 64 + lane];
+      }
+      __syncthreads();
+    }
+    if (wl != 0 || cb >= ncb) continue;
+
+    // Lane holds token row jb + (lane & 15) + 16 g and, for register q, the 8
+    // consecutive output columns n0 + (4 (lane >> 4) + q) * 8 + c, c = 0..7.
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      if (!aval[g]) continue;
+      const int j = jb + (lane & 15) + 16 * g;
+      const size_t orow = UP ? size_t(ks * 2 + mat) * P + slot_of[g]
+                             : (SCAN ? size_t(slot_of[g]) : size_t(rbase + j));
+      float* plane = UP || ks == 0 ? static_cast<float*>(out) : y_part + (ks - 1) * split_stride;
+      float* op = plane + orow * Ndim;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + (4 * (lane >> 4) + q) * 8;
+        if (col >= Ndim) continue;
+        *reinterpret_cast<f32x4*>(op + col) =
+            f32x4{acc[g][0][q], acc[g][1][q], acc[g][2][q], acc[g][3][q]};
+        *reinterpret_cast<f32x4*>(op + col + 4) =
+            f32x4{acc[g][4][q], acc[g][5][q], acc[g][6][q], acc[g][7][q]};
+      }
     }
   }
 }

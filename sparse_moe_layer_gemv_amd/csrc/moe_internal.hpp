@@ -91,9 +91,9 @@ hipError_t launch_route_stats(const Shape& s, const int32_t* topk_idx, int32_t* 
                               hipStream_t stream);
 
 // y_rows[r] += y_part[p * part_stride + r] for p = 0 .. nparts-1 in order, for
-// the rows of the expert segments (r < offset[n]).
-hipError_t launch_add_rows(const Shape& s, const int32_t* expert_offset, float* y_rows,
-                           const float* y_part, int nparts, size_t part_stride,
-                           hipStream_t stream);
+// the rows that hold token-slots (offset[e] <= r < offset[e] + count[e]).
+hipError_t launch_add_rows(const Shape& s, const int32_t* expert_count,
+                           const int32_t* expert_offset, float* y_rows, const float* y_part,
+                           int nparts, size_t part_stride, hipStream_t stream);
 
 }  // namespace moe

@@ -4,8 +4,8 @@ fine-grained layout), in the launch configuration the benchmark times:
 prefill (T=4096: the matrix-core router, the tiled expert path, every expert
 touched) and decode (T=16: the weight-streaming path).
 
-Routing (indices and gates) is checked for every token; the layer output for
-a seeded sample of tokens, which the fp64 oracle evaluates token by token.
+Routing (indices and gates) is checked for every token, and the layer output
+element by element for every token against the fp64 oracle.
 """
 import numpy as np
 import pytest
@@ -15,8 +15,6 @@ from oracle import moe_ref, parity
 from tests.gpu_helpers import dev_bf16, host
 
 pytestmark = pytest.mark.gpu
-
-N_SAMPLE = 48
 
 
 @pytest.fixture(scope="module")
@@ -55,12 +53,10 @@ def _run(moe, name, fine_weights):
     counts = np.bincount(idx_h.ravel(), minlength=w.n)
     print(f"[{name}] routing: {rr} counts min/max={counts.min()}/{counts.max()}")
     assert rr.ok, rr
-    rng = np.random.default_rng(1000 + w.cfg)
-    head, tail = np.arange(min(8, T)), np.arange(max(0, T - 8), T)
-    s = np.unique(np.concatenate([head, tail, rng.choice(T, size=min(T, N_SAMPLE), replace=False)]))
-    ref = moe_ref.moe_layer_rows(x[s], wg, w1, w3, w2, K, forced_idx=rr.forced_idx[s])
-    orep = parity.check_output(ref["y"], out_h[s])
-    print(f"[{name}] sampled {s.size} tokens: max/RMS={orep.max_rel:.3e} mean/RMS={orep.mean_rel:.3e}")
+    ref = moe_ref.moe_layer(x, wg, w1, w3, w2, K, forced_idx=rr.forced_idx)
+    orep = parity.check_output(ref["y"], out_h)
+    print(f"[{name}] all {T} tokens: max/RMS={orep.max_rel:.3e} mean/RMS={orep.mean_rel:.3e}",
+          flush=True)
     assert orep.ok, orep
     return counts
 

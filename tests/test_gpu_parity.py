@@ -177,6 +177,37 @@ def test_route_ties_go_to_the_lower_index_with_many_experts(moe):
     assert np.array_equal(host(idx), want)
 
 
+# T < 2048 takes the vector router (router_kernel), T >= 2048 the matrix-core
+# pair (router_ring_kernel + router_select_kernel) for n = 8
+@pytest.mark.parametrize("T", [64, 1000, 2048, 4096])
+def test_route_ties_go_to_the_lower_index_with_eight_experts(moe, T):
+    # Mixtral's router shape (dim 4096, 8 experts, top-2) with W_g columns 5
+    # and 7 copying columns 2 and 0: their logits are exactly equal, so every
+    # tie the copies make must go to the lower index, with the slots in
+    # decreasing-logit order, and two tied experts chosen together get equal
+    # gates
+    D, n, K = 4096, 8, 2
+    L = moe_synth.make_layer(T, D, 8, n, K, seed=300 + T)
+    wg = L.w_gate.copy()
+    wg[:, 5] = wg[:, 2]
+    wg[:, 7] = wg[:, 0]
+    idx, gate = moe.route(dev_bf16(L.x), dev_bf16(wg), K)
+    idx_h, gate_h = host(idx), host(gate)
+    ref = moe_ref.router_logits(L.x, wg)
+    want = moe_ref.topk_indices(ref, K)
+    assert np.array_equal(idx_h, want)
+    # ties decided here: a copy at the 2nd/3rd boundary lost to its original
+    lost = ((want[:, 1] == 2) & ~np.any(want == 5, axis=1)) | \
+           ((want[:, 1] == 0) & ~np.any(want == 7, axis=1))
+    both = ((want[:, 0] == 2) & (want[:, 1] == 5)) | ((want[:, 0] == 0) & (want[:, 1] == 7))
+    print(f"[ties n=8 T={T}] decided at the boundary: {int(lost.sum())}, "
+          f"both copies chosen: {int(both.sum())}")
+    assert lost.sum() > 0 and both.sum() > 0
+    assert np.all(gate_h[both, 0] == gate_h[both, 1])
+    rr = parity.check_routing(ref, K, idx_h, gate_h)
+    assert rr.gate_max_err <= parity.GATE_TOL, rr
+
+
 def test_permute_drops_out_of_range_experts(moe):
     idx = np.array([[0, 9], [-1, 3], [3, 0]], np.int32)
     r = moe.permute(dev_i32(idx), 8)
@@ -226,6 +257,61 @@ def test_grouped_ffn_forced_routing(moe, label, make, T, D, H):
     out = moe.combine(y_rows, perm["slot_row"], gate)
     want = (ref["gate"].astype(np.float32).astype(np.float64)[:, :, None] * got).sum(axis=1)
     assert np.abs(host(out) - want).max() <= 1e-6 * np.abs(want).max()
+
+
+# A caller's routing may name an expert more than once for one token: each
+# slot is then its own row of that expert.  With every token of a 16-token
+# batch on expert 3 twice (32 rows, more than one 16-row pass of the
+# weight-streaming kernels) or thrice on expert 6 at T = 40 (120 rows, two
+# passes of 64), both expert paths must compute every row.
+@pytest.mark.parametrize("T,K,path", [(16, 2, 1), (16, 2, 2), (40, 3, 1), (40, 3, 2)],
+                         ids=["t16_k2_stream", "t16_k2_tiled", "t40_k3_stream", "t40_k3_tiled"])
+def test_grouped_ffn_repeated_expert_per_token(moe, T, K, path):
+    D, H, n = 512, 1024, 8
+    idx = np.zeros((T, K), np.int32)
+    idx[:, :] = 3 if K == 2 else 6
+    idx[::5, -1] = 1          # a few slots elsewhere
+    L = moe_synth.make_layer(T, D, H, n, K, seed=420 + T)
+    d = _upload(L)
+    perm = moe.permute(dev_i32(idx), n)
+    y_rows = moe.grouped_ffn(d["x"], perm["expert_count"], perm["expert_offset"], perm["row_slot"],
+                             d["w1"], d["w3"], d["w2"], K, path=path)
+    ref = moe_ref.moe_layer(L.x, L.w_gate, L.w1, L.w3, L.w2, K, forced_idx=idx, return_slots=True)
+    sr = host(perm["slot_row"])
+    assert np.all(sr >= 0)
+    got = host(y_rows)[sr].reshape(T, K, D)
+    orep = parity.check_output(ref["E"], got)
+    print(f"[repeat T={T} K={K} path={path}] slots max/RMS={orep.max_rel:.3e} "
+          f"mean/RMS={orep.mean_rel:.3e}")
+    assert orep.ok, orep
+
+
+# moe_grouped_ffn writes the rows that hold token-slots and leaves padding
+# rows as they were, also when the second product's contraction is split and
+# its partials are added afterwards (H = 1024 tiled at T = 900; wide experts
+# streamed at T = 16, 4 partials)
+@pytest.mark.parametrize("T,D,H,path", [(900, 512, 1024, 2), (16, 512, 4096, 1)],
+                         ids=["tiled_split", "stream_split4"])
+def test_grouped_ffn_leaves_padding_rows(moe, T, D, H, path):
+    import torch
+    n, K = 8, 2
+    L = moe_synth.make_layer(T, D, H, n, K, seed=430 + T)
+    d = _upload(L)
+    idx = moe_ref.topk_indices(moe_ref.router_logits(L.x, L.w_gate), K).astype(np.int32)
+    perm = moe.permute(dev_i32(idx), n)
+    cap = moe.capacity_rows(moe.problem(T, D, H, n, K))
+    y_rows = torch.full((cap, D), 777.0, dtype=torch.float32, device="cuda:0")
+    moe.grouped_ffn(d["x"], perm["expert_count"], perm["expert_offset"], perm["row_slot"],
+                    d["w1"], d["w3"], d["w2"], K, y_rows=y_rows, path=path)
+    y = host(y_rows)
+    sr = host(perm["slot_row"])
+    pad = np.ones(cap, bool)
+    pad[sr] = False
+    assert pad.sum() > 0
+    assert np.all(y[pad] == 777.0)
+    ref = moe_ref.moe_layer(L.x, L.w_gate, L.w1, L.w3, L.w2, K, forced_idx=idx, return_slots=True)
+    orep = parity.check_output(ref["E"], y[sr].reshape(T, K, D))
+    assert orep.ok, orep
 
 
 def test_forward_is_deterministic_and_bf16_output_is_rne_of_fp32(moe):
