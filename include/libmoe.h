@@ -223,6 +223,29 @@ moe_status_t moe_route_stats(const moe_problem_t* p, const int32_t* topk_idx, in
  * (decode) path. */
 int32_t moe_decode_max_tokens(void);
 
+/* moe_forward without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same layer, the same kernels and bit-identical
+ * results as moe_forward on its weight-streaming path; every intermediate
+ * lives in a library-owned device array of MOE_NOALLOC_SCRATCH_BYTES that
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates and frees nothing.
+ *   Accepted: the batches moe_forward streams (T <= moe_decode_max_tokens()
+ *   with path AUTO, T <= 64 with path STREAM) whose intermediates fit the
+ *   array: about 4*T*K*(2 + 2*S1*H + S2*D) bytes, S1 = 1 or 2 first-product
+ *   partials, S2 = 1..4 second-product partials (Mixtral's shape, D = 4096,
+ *   H = 14336, K = 2, needs 23 MB at T = 64).  Other shapes, and path TILED,
+ *   return MOE_ENOTSUP with nothing enqueued.
+ *   stream must belong to the calling thread's current device (MOE_EINVAL
+ *   otherwise).
+ * Every call on one GPU uses that GPU's single array and leaves its contents
+ * behind; no part of it needs clearing (a call reads only what it wrote).
+ * Calls that may overlap in time on one GPU (other streams, host threads,
+ * graph branches) race on it: the caller must order them. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* x, const void* w_gate,
+                                 const void* w1, const void* w3, const void* w2, void* out,
+                                 int32_t* topk_idx, float* topk_gate, void* stream);
 
 #ifdef __cplusplus
 }

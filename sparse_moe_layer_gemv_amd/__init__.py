@@ -27,11 +27,13 @@ MOE_F32, MOE_BF16 = 0, 1
 PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
 TILE_M = 256
 MAX_EXPERTS = 256
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 EXPORTED = ("moe_capacity_rows", "moe_workspace_bytes", "moe_status_string", "moe_route",
             "moe_route_workspace_bytes",
             "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-            "moe_decode_max_tokens", "moe_forward_timed", "moe_route_stats")
+            "moe_decode_max_tokens", "moe_forward_timed", "moe_route_stats",
+            "moe_forward_noalloc")
 
 
 for _name in EXPORTED:
@@ -65,8 +67,9 @@ lib.moe_route_stats.argtypes = [_P, _vp, _vp, _vp]
 lib.moe_forward.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 lib.moe_forward_timed.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   _vp, ctypes.POINTER(_vp)]
+lib.moe_forward_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 for _f in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-           "moe_forward_timed", "moe_route_stats"):
+           "moe_forward_timed", "moe_route_stats", "moe_forward_noalloc"):
     getattr(lib, _f).restype = ctypes.c_int32
 
 
@@ -288,4 +291,24 @@ def forward(x, w_gate, w1, w3, w2, top_k: int, out=None, topk_idx=None, topk_gat
             raise ValueError("events must hold 6 hipEvent_t handles")
         arr = (_vp * 6)(*events)
         _check("moe_forward_timed", lib.moe_forward_timed(*args, arr))
+    return out
+
+
+def forward_noalloc(x, w_gate, w1, w3, w2, top_k: int, out, topk_idx=None, topk_gate=None,
+                    out_dtype: int = MOE_F32, stream=None, path: int = PATH_AUTO):
+    """moe_forward_noalloc: the whole layer with no workspace (the library's
+    own device array holds the intermediates).  For the batches moe_forward
+    streams; `out` (and the optional routing outputs) must be given, since
+    this call is for callers that do not allocate.  Returns out."""
+    torch = _torch()
+    p = _shape_of(x, w1, top_k, out_dtype, path)
+    T, D, H, n = p.tokens, p.dim, p.hidden, p.n_experts
+    _check("moe_forward_noalloc", lib.moe_forward_noalloc(
+        ctypes.byref(p), _ptr(x, _bf16(), (T, D), "x"), _ptr(w_gate, _bf16(), (D, n), "w_gate"),
+        _ptr(w1, _bf16(), (n, D, H), "w1"), _ptr(w3, _bf16(), (n, D, H), "w3"),
+        _ptr(w2, _bf16(), (n, H, D), "w2"),
+        _ptr(out, (torch.float32,) if out_dtype == MOE_F32 else _bf16(), (T, D), "out"),
+        _ptr(topk_idx, torch.int32, (T, top_k), "topk_idx", optional=True),
+        _ptr(topk_gate, torch.float32, (T, top_k), "topk_gate", optional=True),
+        _stream(stream)))
     return out

@@ -6,7 +6,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <functional>
+#include <mutex>
 
 #include "moe_internal.hpp"
 
@@ -97,6 +99,58 @@ Carve carve(const Shape& s) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// ---------------------------------------------------------------------------
+// Allocation-free forward (moe_forward_noalloc): its intermediates live in
+// `scratch`, a library-owned array that every GPU the library runs on holds
+// from module load until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels only ever get the address
+// hipGetSymbolAddress returns for the current device.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(MOE_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the calling thread's current device, looked
+// up once per device (devices 0..63) and kept; nullptr if the lookup fails.
+uint8_t* static_scratch(int dev) {
+  constexpr int kDevices = 64;
+  static std::atomic<void*> addr[kDevices];
+  static std::mutex mu;
+  if (dev < 0 || dev >= kDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  return static_cast<uint8_t*>(p);
+}
+
+// Layout of the weight-streaming path without a permute pass, rows indexed
+// by slot (P = T*K rows per plane): routing, the fp32 first products and the
+// second product's partials (the router's partial logits, when it needs
+// them, at the start of the y region, consumed before y is written).
+struct CompactCarve {
+  size_t idx, gate, ab, y, total;
+  int planes;
+};
+
+CompactCarve compact_carve(const Shape& s) {
+  CompactCarve c{};
+  const size_t P = size_t(s.T) * s.K;
+  size_t o = 0;
+  c.idx = o;  o = align_up(o + P * 4, kAlign);
+  c.gate = o; o = align_up(o + P * 4, kAlign);
+  c.ab = o;   o = align_up(o + moe::decode_scratch_bytes(s), kAlign);
+  c.planes = moe::decode_down_splits(s);
+  c.y = o;
+  o = align_up(o + std::max(size_t(c.planes) * P * s.D * 4, moe::route_scratch_bytes(s)), kAlign);
+  c.total = o;
+  return c;
+}
+
 bool use_decode(const Shape& s) { return s.stream; }
 
 // `mark(i)`, when given, records stage event i (3 after the first product, 4
@@ -108,10 +162,13 @@ using MarkFn = std::function<hipError_t(int)>;
 // With `topk_idx` (weight-streaming path only) the experts' token-slots are
 // read from the routing and the rows land at the slot index; otherwise the
 // permuted layout (count, offset, row_slot) gives them.
+// part_stride: floats between consecutive partials of the streaming path's
+// second product (partial p >= 1 at y_part + (p - 1) * part_stride).
 moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const int32_t* offset,
                      const int32_t* row_slot, const int32_t* topk_idx, const void* w1,
-                     const void* w3, const void* w2, float* y_rows, float* y_part, int* nsplit,
-                     uint16_t* h, hipStream_t st, const MarkFn& mark = nullptr) {
+                     const void* w3, const void* w2, float* y_rows, float* y_part,
+                     size_t part_stride, int* nsplit, uint16_t* h, hipStream_t st,
+                     const MarkFn& mark = nullptr) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* w1b = static_cast<const uint16_t*>(w1);
   const uint16_t* w3b = static_cast<const uint16_t*>(w3);
@@ -127,7 +184,7 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   if (use_decode(s)) {
     *nsplit = y_part ? moe::decode_down_splits(s) : 1;
     e = moe::launch_decode_down(s, count, offset, row_slot, topk_idx, ab, w2b, y_rows, y_part,
-                                *nsplit, size_t(s.cap) * s.D, st);
+                                *nsplit, part_stride, st);
   } else {
     *nsplit = y_part ? moe::grouped_down_splits(s) : 1;
     e = moe::launch_grouped_down(s, count, offset, h, w2b, y_rows, *nsplit, y_part, st);
@@ -229,7 +286,7 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_
   // a split second product leaves its partials beyond the first in the
   // workspace; they are added into y_rows in order
   st = run_ffn(s, x, expert_count, expert_offset, row_slot, nullptr, w1, w3, w2, y_rows, y_part,
-               &nsplit, reinterpret_cast<uint16_t*>(base + c.h), hs);
+               size_t(s.cap) * s.D, &nsplit, reinterpret_cast<uint16_t*>(base + c.h), hs);
   if (st != MOE_OK || nsplit == 1) return st;
   return hip_status(moe::launch_add_rows(s, expert_count, expert_offset, y_rows, y_part,
                                          nsplit - 1, size_t(s.cap) * s.D, hs));
@@ -312,13 +369,53 @@ moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void
   const size_t part_stride = size_t(s.cap) * s.D;
   int nsplit = 1;
   st = run_ffn(s, x, count, offset, row_slot, scan ? idx : nullptr, w1, w3, w2, y,
-               y + part_stride, &nsplit, h, hs, events ? MarkFn(mark) : MarkFn());
+               y + part_stride, part_stride, &nsplit, h, hs, events ? MarkFn(mark) : MarkFn());
   if (st != MOE_OK) return st;
   if (moe::launch_combine(s, y, nsplit, part_stride, scan ? nullptr : slot_row, idx, gate, out,
                           p->out_dtype == MOE_BF16, hs) != hipSuccess ||
       mark(5) != hipSuccess)
     return MOE_EHIP;
   return MOE_OK;
+}
+
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* x, const void* w_gate,
+                                 const void* w1, const void* w3, const void* w2, void* out,
+                                 int32_t* topk_idx, float* topk_gate, void* stream) {
+  Shape s;
+  moe_status_t st = check_problem(p, &s);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_gate || !w1 || !w3 || !w2 || !out) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w1) || !aligned16(w3) ||
+      !aligned16(w2) || !aligned16(out) || (topk_idx && !aligned16(topk_idx)) ||
+      (topk_gate && !aligned16(topk_gate)))
+    return MOE_EINVAL;
+  // only the weight-streaming path, whose intermediates are small
+  if (!s.stream) return MOE_ENOTSUP;
+  const CompactCarve c = compact_carve(s);
+  if (c.total > kStaticScratchBytes) return MOE_ENOTSUP;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || hipStreamGetDevice(hs, &sdev) != hipSuccess)
+    return MOE_EHIP;
+  if (sdev != dev) return MOE_EINVAL;  // the array's address is the current device's
+  uint8_t* base = static_scratch(dev);
+  if (!base) return MOE_EHIP;
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(base + c.idx);
+  float* gate = topk_gate ? topk_gate : reinterpret_cast<float*>(base + c.gate);
+  float* ab = reinterpret_cast<float*>(base + c.ab);
+  float* y = reinterpret_cast<float*>(base + c.y);
+  const size_t part_stride = size_t(s.T) * s.K * s.D;
+  if (moe::launch_route(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate),
+                        idx, gate, nullptr, y, hs) != hipSuccess)
+    return MOE_EHIP;
+  int nsplit = 1;
+  st = run_ffn(s, x, nullptr, nullptr, nullptr, idx, w1, w3, w2, y, y + part_stride, part_stride,
+               &nsplit, reinterpret_cast<uint16_t*>(ab), hs);
+  if (st != MOE_OK) return st;
+  // nsplit == c.planes: the second product's partials fill the y planes
+  return hip_status(moe::launch_combine(s, y, nsplit, part_stride, nullptr, idx, gate, out,
+                                        p->out_dtype == MOE_BF16, hs));
 }
 
 }  // extern "C"
