@@ -9,7 +9,11 @@ HBM.  Workloads (seeded, see moe_synth): prefill (T=4096, the default), decode
 fed as 4 chunks of 8192 through one workspace), tiny, and the fine-grained
 layout fine_prefill / fine_decode (8 of 160 experts of width 768, T=4096 / 16).
 
-Prints one JSON line.  Every 4th timed step records HIP events on the
+Prints one JSON line: the headline workload (--workload, prefill by default)
+at the top level and, unless --no-side, one sub-record per other workload
+under "workloads" (decode, skewed, large, tiny, fine_prefill, fine_decode;
+fewer steps each), each with its time, throughput, stage breakdown and the
+dominant kernel's roofline.  Every 4th timed step records HIP events on the
 layer's stream around the dominant kernel (the first expert product: x.w1,
 x.w3 + silu), whose event-timed average launch the roofline object uses; the
 per-stage breakdown comes from a separate pass with every stage boundary
@@ -279,53 +283,21 @@ def stages_alone(args, torch, moe):
     return 0
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=sorted(moe_synth.WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=0,
-                    help="tokens for the oracle timing (default: a bounded sample per workload)")
-    ap.add_argument("--crossover", action="store_true",
-                    help="small-batch sweep: time both expert-product paths for T = 1..256 and "
-                         "print one JSON line with the measured crossover")
-    ap.add_argument("--stages", action="store_true",
-                    help="router, permute and combine each timed alone at the workload's shape, "
-                         "over rotating inputs of at least 1 GiB (one JSON line)")
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "libmoe is a single-GPU build: each GPU runs the whole layer "
-                                   "on its own share of tokens and there is no cross-GPU step; "
-                                   "run with --gpus 1"}))
-        return 2
-
-    import torch
-    import sparse_moe_layer_gemv_amd as moe
-    from sparse_moe_layer_gemv_amd.profiling import load_traffic
-
-    if args.crossover:
-        return crossover(args, torch, moe)
-    if args.stages:
-        return stages_alone(args, torch, moe)
-
-    w = moe_synth.WORKLOADS[args.workload]
+def time_workload(name, L, dev, steps, warmup, torch, moe, load_traffic, ev):
+    """Time `steps` layer passes of workload `name` (after `warmup` untimed
+    ones) on inputs already in HBM.  dev: the uploaded x, w_gate, w1, w3, w2.
+    Returns the per-workload record (time, throughput, stage breakdown and
+    the dominant kernel's roofline)."""
+    w = moe_synth.WORKLOADS[name]
     T, D, H, n, K = w.T, w.D, w.H, w.n, w.K
     chunk = w.chunk or T
-    log(f"[bench] generating {args.workload} inputs T={T} D={D} H={H} n={n} K={K}")
-    t0 = time.perf_counter()
-    L = moe_synth.make_workload(args.workload)
-    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
-    x, wg, w1, w3, w2 = (to_dev(a) for a in (L.x, L.w_gate, L.w1, L.w3, L.w2))
+    x, wg, w1, w3, w2 = dev
     out = torch.empty((T, D), dtype=torch.float32, device="cuda:0")
     idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
     gate = torch.empty((T, K), dtype=torch.float32, device="cuda:0")
     ws = torch.empty(moe.workspace_bytes(moe.problem(chunk, D, H, n, K)), dtype=torch.uint8,
                      device="cuda:0")
     stream = torch.cuda.current_stream()
-    ev = HipEvents()
     n_chunks = (T + chunk - 1) // chunk
 
     def step(events_for_step=None):
@@ -335,31 +307,31 @@ def main(argv=None):
             moe.forward(x[c0:c1], wg, w1, w3, w2, K, out=out[c0:c1], topk_idx=idx[c0:c1],
                         topk_gate=gate[c0:c1], workspace=ws, stream=stream, events=e6)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+    log(f"[bench] {name}: warmup done ({warmup} steps); timing {steps} steps")
 
     # Every recorded event costs the stream a few microseconds, so the timed
     # steps record only the two events around the first expert product (the
     # dominant kernel, whose launches the roofline needs timed live), and only
     # on every EVENT_EVERY-th step; the other stage boundaries are taken in a
     # separate pass afterwards.
-    sampled = list(range(0, args.steps, EVENT_EVERY))
+    sampled = list(range(0, steps, EVENT_EVERY))
     up_evs = {s: [ev.create(2) for _ in range(n_chunks)] for s in sampled}
     timed = [[[None, None, e2[0], e2[1], None, None] for e2 in up_evs[s]] if s in up_evs else None
-             for s in range(args.steps)]
+             for s in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(timed[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    log(f"[bench] timed region done: {wall * 1e3:.2f} ms")
+    log(f"[bench] {name}: timed region done: {wall * 1e3:.2f} ms")
     up_timed = [ev.elapsed_ms(e2[0], e2[1]) for s in sampled for e2 in up_evs[s]]
 
     # stage breakdown: all six events, in a pass of its own
-    prof_steps = max(1, min(args.steps, 10))
+    prof_steps = max(1, min(steps, 10))
     evs = [[ev.create(6) for _ in range(n_chunks)] for _ in range(prof_steps)]
     for s in range(prof_steps):
         step(evs[s])
@@ -380,18 +352,17 @@ def main(argv=None):
     stage_avg = {k: float(np.mean(v)) for k, v in stage_ms.items()}
     up_avg_timed = float(np.mean(up_timed))
 
-    ms_per_step = wall * 1e3 / args.steps
-    tokens_per_s = T / (ms_per_step / 1e3)
+    ms_per_step = wall * 1e3 / steps
     flops = layer_flops(T, D, H, n, K)
     tflops = flops / (ms_per_step / 1e3) / 1e12
 
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=n)
     touched = int((counts > 0).sum())
-    decode = T <= moe.decode_max_tokens()
+    decode = chunk <= moe.decode_max_tokens()
     kernel = "decode_up" if decode else "grouped_up"
     # HBM bytes per launch from the stored counter runs of this exact kernel
     # source (None once the source has changed since they were taken)
-    tr = load_traffic(kernel, args.workload)
+    tr = load_traffic(kernel, name)
     traffic = None if tr is None else tr["bytes_per_launch"]
     # The dominant kernel's bound: the larger of its time at the matrix-core
     # peak (algorithmic FLOPs) and at the HBM peak (algorithmic bytes: w1 and
@@ -421,20 +392,10 @@ def main(argv=None):
     roof["kernel_launches_timed"] = len(up_timed)
 
     rec = {
-        "metric": METRIC,
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "workload": name, "tokens": T, "dim": D, "hidden": H, "n_experts": n, "top_k": K,
+        "chunk": chunk, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "dim": D, "hidden": H,
-                   "n_experts": n, "top_k": K, "chunk": chunk, "parallelism": "none"},
+        "tokens_per_s": T / (ms_per_step / 1e3),
         "tflops": tflops,
         "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
         # per-stage breakdown and event-timed layer time from the separate pass
@@ -447,14 +408,115 @@ def main(argv=None):
         "roofline": roof,
     }
     if decode:
+        # the whole layer against HBM: every touched expert's three matrices
+        # once, plus x, W_g, out and the routing
         total_bytes = touched * 3 * D * H * 2 + T * D * 2 + D * n * 2 + T * D * 4 + T * K * 8
         rec["hbm_gbs_layer"] = total_bytes / (ms_per_step / 1e3) / 1e9
         rec["hbm_peak_frac_layer"] = rec["hbm_gbs_layer"] / PEAK_HBM_GBS
+    return rec
+
+
+# Workloads timed beside the headline one in the default run, with the steps
+# each gets (a step of `large` is 4 layer calls of 8192 tokens).
+SIDE_WORKLOADS = (("decode", 50), ("skewed", 30), ("large", 10), ("tiny", 50),
+                  ("fine_prefill", 30), ("fine_decode", 50))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=sorted(moe_synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="time only the headline workload (no per-workload sub-records)")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens for the oracle timing (default: a bounded sample per workload)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="small-batch sweep: time both expert-product paths for T = 1..256 and "
+                         "print one JSON line with the measured crossover")
+    ap.add_argument("--stages", action="store_true",
+                    help="router, permute and combine each timed alone at the workload's shape, "
+                         "over rotating inputs of at least 1 GiB (one JSON line)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "libmoe is a single-GPU build: each GPU runs the whole layer "
+                                   "on its own share of tokens and there is no cross-GPU step; "
+                                   "run with --gpus 1"}))
+        return 2
+
+    import torch
+    import sparse_moe_layer_gemv_amd as moe
+    from sparse_moe_layer_gemv_amd.profiling import load_traffic
+
+    if args.crossover:
+        return crossover(args, torch, moe)
+    if args.stages:
+        return stages_alone(args, torch, moe)
+
+    names = [args.workload]
+    side = {}
+    if not args.no_side:
+        side = {nm: min(st, args.steps) for nm, st in SIDE_WORKLOADS if nm != args.workload}
+        names += list(side)
+    # one upload per weight set: the Mixtral-shape workloads share theirs
+    uploaded = {}
+    records = {}
+    head_inputs = None
+    for name in names:
+        w = moe_synth.WORKLOADS[name]
+        log(f"[bench] generating {name} inputs T={w.T} D={w.D} H={w.H} n={w.n} K={w.K}")
+        t0 = time.perf_counter()
+        L = moe_synth.make_workload(name)
+        log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+        key = (w.weight_seed, w.D, w.H, w.n)
+        if key not in uploaded:
+            uploaded.clear()  # the previous weight set is no longer needed
+            torch.cuda.empty_cache()
+            uploaded[key] = tuple(to_dev(a) for a in (L.w1, L.w3, L.w2))
+        dev = (to_dev(L.x), to_dev(L.w_gate)) + uploaded[key]
+        steps = args.steps if name == args.workload else side[name]
+        warmup = args.warmup if name == args.workload else min(args.warmup, 3)
+        records[name] = time_workload(name, L, dev, steps, warmup, torch, moe, load_traffic,
+                                      HipEvents())
+        del dev
+        if name == args.workload:
+            head_inputs = L
+        else:
+            del L
+
+    h = records[args.workload]
+    rec = {
+        "metric": METRIC,
+        "value": h["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": h["tokens"], "dim": h["dim"],
+                   "hidden": h["hidden"], "n_experts": h["n_experts"], "top_k": h["top_k"],
+                   "chunk": h["chunk"], "parallelism": "none"},
+    }
+    for k in ("tflops", "mfma_peak_frac", "stage_ms", "step_gpu_ms", "stage_pass_steps",
+              "expert_counts", "roofline", "hbm_gbs_layer", "hbm_peak_frac_layer"):
+        if k in h:
+            rec[k] = h[k]
+    if side:
+        rec["workloads"] = {nm: r for nm, r in records.items() if nm != args.workload}
 
     if not args.no_cpu_baseline:
+        T = moe_synth.WORKLOADS[args.workload].T
         sample = args.cpu_sample or min(T, 4096)
         log(f"[bench] timing the fp64 oracle on {sample} tokens")
-        rec["cpu_baseline"] = cpu_baseline(args.workload, L, sample)
+        rec["cpu_baseline"] = cpu_baseline(args.workload, head_inputs, sample)
     print(json.dumps(rec), flush=True)
     return 0
 

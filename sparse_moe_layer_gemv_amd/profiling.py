@@ -175,6 +175,92 @@ def cmd_traffic(a) -> int:
     return 0
 
 
+# bf16 dense matrix-core rate of one compute unit per clock (MI355X: 2.5 PF/s
+# published = 256 CUs x 4096 FLOP/clk x 2.4 GHz)
+BF16_FLOP_PER_CU_CLK = 4096
+N_CU = 256
+SIMD_PER_CU = 4
+
+
+def read_counters(d: str, name_regex: str):
+    """{dispatch: {"kernel", "dur_us", counter: value}} for kernels matching name_regex."""
+    out = {}
+    with open(_counter_csv(d)) as f:
+        for r in csv.DictReader(f):
+            if not re.search(name_regex, r["Kernel_Name"]):
+                continue
+            i = int(r["Dispatch_Id"])
+            rec = out.setdefault(i, {"kernel": _short(r["Kernel_Name"]),
+                                     "dur_us": (int(r["End_Timestamp"]) -
+                                                int(r["Start_Timestamp"])) / 1e3})
+            rec[r["Counter_Name"]] = rec.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return dict(sorted(out.items()))
+
+
+def cmd_mfma(a) -> int:
+    """Matrix-core evidence of one kernel from a --pmc run of SQ_INSTS_VALU_MFMA_MOPS_BF16
+    (bf16 MFMA work in units of 512 FLOP), SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE: FLOPs issued (padding rows included) against the algorithmic
+    count, the achieved rate, the clock GRBM_GUI_ACTIVE / duration implies, and the
+    fraction of the matrix-core peak at that clock."""
+    rows = read_counters(a.dir, a.regex)
+    if not rows:
+        raise RuntimeError("no dispatch of the kernel in the counter run")
+    keys = [k for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES",
+                        "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE") if k in next(iter(rows.values()))]
+    lines = [f"# Matrix-core counters, `{a.kernel}` on the {a.workload} workload", "",
+             "Command (on the MI355X box, from the repository root; $REPO is the repository path):",
+             "", "```", "cd /tmp && export TMPDIR=/tmp"] + a.command + ["```", "",
+             "| dispatch | kernel | duration (us) | " + " | ".join(keys) + " |",
+             "|---|---|---|" + "---|" * len(keys)]
+    for i, r in rows.items():
+        lines.append(f"| {i} | `{r['kernel']}` | {r['dur_us']:.1f} | " +
+                     " | ".join(f"{r.get(k, 0):.0f}" for k in keys) + " |")
+    steady = list(rows.values())[1:] or list(rows.values())
+    med = {k: statistics.median([r.get(k, 0.0) for r in steady]) for k in keys + ["dur_us"]}
+    dur = med["dur_us"] * 1e-6
+    summary = {"kernel": a.kernel, "workload": a.workload, "dispatches": len(rows),
+               "duration_us": med["dur_us"], "algorithmic_flop": a.algorithmic_flop,
+               "raw_median": {k: med[k] for k in keys}, "grbm_scale": a.grbm_scale}
+    lines += ["", "Medians over the dispatches after the first:", ""]
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+        flop = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        summary.update(issued_flop=flop, issued_tflops=flop / dur / 1e12,
+                       issued_over_algorithmic=flop / a.algorithmic_flop if a.algorithmic_flop else None)
+        lines.append(f"- bf16 matrix-core work issued: {flop / 1e12:.4f} TFLOP "
+                     f"({flop / a.algorithmic_flop:.4f} x the algorithmic {a.algorithmic_flop / 1e12:.4f}"
+                     " TFLOP; the excess is padding rows)" if a.algorithmic_flop else "")
+        lines.append(f"- issued rate: {flop / dur / 1e12:.1f} TFLOP/s; algorithmic rate "
+                     f"{a.algorithmic_flop / dur / 1e12:.1f} TFLOP/s "
+                     f"({a.algorithmic_flop / dur / 1e12 / 2500:.3f} of the published 2.5 PF/s)")
+    if "GRBM_GUI_ACTIVE" in med:
+        cycles = med["GRBM_GUI_ACTIVE"] / a.grbm_scale
+        clk = cycles / dur
+        summary.update(gpu_cycles=cycles, clock_ghz=clk / 1e9)
+        lines.append(f"- GRBM_GUI_ACTIVE / {a.grbm_scale:g} = {cycles:.0f} cycles over "
+                     f"{med['dur_us']:.1f} us: {clk / 1e9:.3f} GHz")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+            peak_at_clk = N_CU * BF16_FLOP_PER_CU_CLK * cycles
+            summary["issued_over_peak_at_clock"] = flop / peak_at_clk
+            lines.append(f"- issued work over the matrix-core peak at that clock "
+                         f"({N_CU} CUs x {BF16_FLOP_PER_CU_CLK} FLOP/clk x {cycles:.0f} cycles): "
+                         f"{flop / peak_at_clk:.3f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            # the busy count is summed over the SIMDs (4 per CU), each of
+            # which owns a matrix core
+            busy = med["SQ_VALU_MFMA_BUSY_CYCLES"]
+            simds = N_CU * SIMD_PER_CU
+            summary["mfma_busy_over_simd_cycles"] = busy / (cycles * simds)
+            lines.append(f"- SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {simds} SIMDs): "
+                         f"{busy / (cycles * simds):.3f} of the matrix cores' cycles busy")
+    lines += ["", "```json", json.dumps(summary, indent=1), "```", ""]
+    out = os.path.join(PROFILES, f"mfma_{a.kernel}_{a.workload}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(l for l in lines if l is not None) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def cmd_stats(a) -> int:
     with open(a.csv) as f:
         rows = list(csv.DictReader(f))
@@ -207,13 +293,22 @@ def main(argv=None) -> int:
     t.add_argument("--cal-fetch", required=True, help="FETCH_SIZE run of the calibration copy")
     t.add_argument("--cal-write", required=True, help="WRITE_SIZE run of the calibration copy")
     t.add_argument("--command", action="append", default=[], help="command line to record")
+    m = sub.add_parser("mfma", help="matrix-core counters -> profiles/mfma_<kernel>_<workload>.md")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--regex", required=True)
+    m.add_argument("--dir", required=True, help="rocprofv3 -d folder of the counter run")
+    m.add_argument("--algorithmic-flop", type=float, default=0.0)
+    m.add_argument("--grbm-scale", type=float, default=1.0,
+                   help="divide GRBM_GUI_ACTIVE by this (instances summed into the counter)")
+    m.add_argument("--command", action="append", default=[])
     s = sub.add_parser("stats", help="rocprofv3 --stats csv -> markdown")
     s.add_argument("--csv", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
-    return {"copy": cmd_copy, "traffic": cmd_traffic, "stats": cmd_stats}[a.cmd](a)
+    return {"copy": cmd_copy, "traffic": cmd_traffic, "mfma": cmd_mfma, "stats": cmd_stats}[a.cmd](a)
 
 
 if __name__ == "__main__":
