@@ -175,10 +175,11 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   const uint16_t* w2b = static_cast<const uint16_t*>(w2);
   hipError_t e;
   float* ab = reinterpret_cast<float*>(h);  // decode: fp32 first products
-  if (use_decode(s))
+  if (use_decode(s)) {
     e = moe::launch_decode_up(s, xb, count, offset, row_slot, topk_idx, w1b, w3b, ab, st);
-  else
-    e = moe::launch_grouped_up(s, xb, offset, row_slot, w1b, w3b, h, st);
+  } else {
+    e = moe::launch_grouped_up(s, xb, count, offset, row_slot, w1b, w3b, h, st);
+  }
   if (e != hipSuccess || (mark && mark(3) != hipSuccess)) return MOE_EHIP;
   *nsplit = 1;
   if (use_decode(s)) {

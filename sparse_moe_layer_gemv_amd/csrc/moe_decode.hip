@@ -131,7 +131,15 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     cnt = expert_count[e];
     rbase = expert_offset[e];
   }
-  if (cnt == 0) return;
+  // Pass blockIdx.y covers the expert's token rows [16 RG y, 16 RG (y + 1)).
+  // RG is chosen from T, and an expert holds at most T rows when every token
+  // names it at most once (always so under moe_forward, whose router picks K
+  // distinct experts, and the only case SCAN serves); a caller's layout for
+  // moe_grouped_ffn may name an expert twice for one token, and its rows
+  // beyond the first pass are then taken by the further passes of the grid,
+  // whose workgroups otherwise exit here.
+  const int jb = blockIdx.y * 16 * RG;
+  if (cnt <= jb) return;
   const int n0 = cb * 128;
   const int kg = lane >> 4;
   const int nbk = lane & 15;
@@ -139,134 +147,123 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   const int kbeg = ks * klen;
   const int kend = min(Kdim, kbeg + klen);
   const size_t ab_stride = size_t(2) * P * Kdim;   // DOWN: floats between ab partials
+
+  // activation row pointers (token row j = jb + lane % 16 + 16 g of the expert)
+  const uint16_t* xrow[RG];
+  const float* arow[RG];
+  const float* brow[RG];
+  bool aval[RG];
+  int slot_of[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const int j = jb + (lane & 15) + 16 * g;
+    aval[g] = j < cnt;
+    int slot = 0;
+    if (aval[g]) {
+      if constexpr (SCAN) {
+        slot = s_list[j];
+      } else {
+        slot = row_slot[rbase + j];
+      }
+    }
+    slot_of[g] = slot;
+    const int sl = slot >= 0 ? slot : 0;
+    if (UP) {
+      xrow[g] = x + size_t(sl / topk) * Kdim;
+    } else {
+      arow[g] = ab + size_t(sl) * Kdim;
+      brow[g] = ab + (size_t(P) + sl) * Kdim;
+    }
+  }
   const uint16_t* wp =
       (UP && mat ? w1 : w0) + size_t(e) * Kdim * Ndim + (cb < ncb ? n0 : 0) + nbk * 8;
+
+  f32x4 acc[RG][8];
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[g][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   const int steps = (kend - kbeg + 31) / 32;
   const int per = (steps + WPG - 1) / WPG;
   const int s0 = wl * per;
   const int s1 = min(steps, s0 + per);
-
-  // Passes of 16 RG token rows.  RG is chosen from T, and an expert holds at
-  // most T rows when every token names it at most once (always so under
-  // moe_forward, whose router picks K distinct experts); a caller's layout
-  // for moe_grouped_ffn may name an expert twice for one token, and then the
-  // rows beyond the first pass take further passes over the weights.  cnt
-  // is uniform over the workgroup, so every wave runs the same passes (the
-  // reduction's barriers).
-  for (int jb = 0; jb < cnt; jb += 16 * RG) {
-    // activation row pointers (token row j = jb + lane % 16 + 16 g of the expert)
-    const uint16_t* xrow[RG];
-    const float* arow[RG];
-    const float* brow[RG];
-    bool aval[RG];
-    int slot_of[RG];
+  for (int s = s0; s < s1; ++s) {
+    const int kk = kbeg + s * 32 + kg * 8;
+    const bool kok = kk < kend;
+    uint4 wv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      wv[j] = (kok && col_ok) ? load_weight(wp + size_t(kk + j) * Ndim) : make_uint4(0, 0, 0, 0);
+    bf16x8 xv[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-      const int j = jb + (lane & 15) + 16 * g;
-      aval[g] = j < cnt;
-      int slot = 0;
-      if (aval[g]) {
-        if constexpr (SCAN) {
-          slot = s_list[j];
-        } else {
-          slot = row_slot[rbase + j];
-        }
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kok && aval[g]) {
+        if (UP)
+          v = *reinterpret_cast<const uint4*>(xrow[g] + kk);
+        else
+          v = h_fragment(arow[g] + kk, brow[g] + kk, ab_parts, ab_stride);
       }
-      slot_of[g] = slot;
-      const int sl = slot >= 0 ? slot : 0;
-      if (UP) {
-        xrow[g] = x + size_t(sl / topk) * Kdim;
-      } else {
-        arow[g] = ab + size_t(sl) * Kdim;
-        brow[g] = ab + (size_t(P) + sl) * Kdim;
-      }
+      xv[g] = as_bf16x8(v);
     }
+    uint4 op[8];
+    transpose8x8_bf16(wv, op);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        acc[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op[c]), xv[g], acc[g][c], 0, 0, 0);
+  }
 
-    f32x4 acc[RG][8];
+  // Tree reduction over each group's waves: at each level the upper half
+  // stores, the lower half adds.  Group g uses slots [g WPG/2, (g+1) WPG/2).
+  // Layout [slot][value][lane] keeps every store/load bank-clean.
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
+  for (int half = WPG / 2; half >= 1; half >>= 1) {
+    if (wl >= half && wl < 2 * half) {
+      float* dst = red + size_t(grp * (WPG / 2) + wl - half) * NACC * 4 * 64;
+      int v = 0;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[g][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = s0; s < s1; ++s) {
-      const int kk = kbeg + s * 32 + kg * 8;
-      const bool kok = kk < kend;
-      uint4 wv[8];
+      for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        wv[j] = (kok && col_ok) ? load_weight(wp + size_t(kk + j) * Ndim) : make_uint4(0, 0, 0, 0);
-      bf16x8 xv[RG];
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int g = 0; g < RG; ++g) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (kok && aval[g]) {
-          if (UP)
-            v = *reinterpret_cast<const uint4*>(xrow[g] + kk);
-          else
-            v = h_fragment(arow[g] + kk, brow[g] + kk, ab_parts, ab_stride);
-        }
-        xv[g] = as_bf16x8(v);
-      }
-      uint4 op[8];
-      transpose8x8_bf16(wv, op);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int g = 0; g < RG; ++g)
-          acc[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op[c]), xv[g], acc[g][c], 0, 0, 0);
+          for (int q = 0; q < 4; ++q, ++v) dst[v * 64 + lane] = acc[g][c][q];
     }
-
-    // Tree reduction over each group's waves: at each level the upper half
-    // stores, the lower half adds.  Group g uses slots [g WPG/2, (g+1) WPG/2).
-    // Layout [slot][value][lane] keeps every store/load bank-clean.  The
-    // barrier closing each level also orders this pass's last reads of `red`
-    // before the next pass's first stores.
+    __syncthreads();
+    if (wl < half) {
+      const float* src = red + size_t(grp * (WPG / 2) + wl) * NACC * 4 * 64;
+      int v = 0;
 #pragma unroll
-    for (int half = WPG / 2; half >= 1; half >>= 1) {
-      if (wl >= half && wl < 2 * half) {
-        float* dst = red + size_t(grp * (WPG / 2) + wl - half) * NACC * 4 * 64;
-        int v = 0;
+      for (int g = 0; g < RG; ++g)
 #pragma unroll
-        for (int g = 0; g < RG; ++g)
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-          for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int q = 0; q < 4; ++q, ++v) dst[v * 64 + lane] = acc[g][c][q];
-      }
-      __syncthreads();
-      if (wl < half) {
-        const float* src = red + size_t(grp * (WPG / 2) + wl) * NACC * 4 * 64;
-        int v = 0;
-#pragma unroll
-        for (int g = 0; g < RG; ++g)
-#pragma unroll
-          for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int q = 0; q < 4; ++q, ++v) acc[g][c][q] += src[v * 64 + lane];
-      }
-      __syncthreads();
+          for (int q = 0; q < 4; ++q, ++v) acc[g][c][q] += src[v * 64 + lane];
     }
-    if (wl != 0 || cb >= ncb) continue;
+    __syncthreads();
+  }
+  if (wl != 0 || cb >= ncb) return;
 
-    // Lane holds token row jb + (lane & 15) + 16 g and, for register q, the 8
-    // consecutive output columns n0 + (4 (lane >> 4) + q) * 8 + c, c = 0..7.
+  // Lane holds token row jb + (lane & 15) + 16 g and, for register q, the 8
+  // consecutive output columns n0 + (4 (lane >> 4) + q) * 8 + c, c = 0..7.
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      if (!aval[g]) continue;
-      const int j = jb + (lane & 15) + 16 * g;
-      const size_t orow = UP ? size_t(ks * 2 + mat) * P + slot_of[g]
-                             : (SCAN ? size_t(slot_of[g]) : size_t(rbase + j));
-      float* plane = UP || ks == 0 ? static_cast<float*>(out) : y_part + (ks - 1) * split_stride;
-      float* op = plane + orow * Ndim;
+  for (int g = 0; g < RG; ++g) {
+    if (!aval[g]) continue;
+    const int j = jb + (lane & 15) + 16 * g;
+    const size_t orow = UP ? size_t(ks * 2 + mat) * P + slot_of[g]
+                           : (SCAN ? size_t(slot_of[g]) : size_t(rbase + j));
+    float* plane = UP || ks == 0 ? static_cast<float*>(out) : y_part + (ks - 1) * split_stride;
+    float* op = plane + orow * Ndim;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + (4 * (lane >> 4) + q) * 8;
-        if (col >= Ndim) continue;
-        *reinterpret_cast<f32x4*>(op + col) =
-            f32x4{acc[g][0][q], acc[g][1][q], acc[g][2][q], acc[g][3][q]};
-        *reinterpret_cast<f32x4*>(op + col + 4) =
-            f32x4{acc[g][4][q], acc[g][5][q], acc[g][6][q], acc[g][7][q]};
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int col = n0 + (4 * (lane >> 4) + q) * 8;
+      if (col >= Ndim) continue;
+      *reinterpret_cast<f32x4*>(op + col) =
+          f32x4{acc[g][0][q], acc[g][1][q], acc[g][2][q], acc[g][3][q]};
+      *reinterpret_cast<f32x4*>(op + col + 4) =
+          f32x4{acc[g][4][q], acc[g][5][q], acc[g][6][q], acc[g][7][q]};
     }
   }
 }
@@ -304,8 +301,13 @@ hipError_t launch_decode_nb(const Shape& s, const uint16_t* x, const float* ab,
                             size_t split_stride, int ab_parts, hipStream_t stream) {
   const int ncb = (Ndim + 127) / 128;
   const int groups = (ncb + NB - 1) / NB;
-  const dim3 grid(s.n * groups * (UP ? 2 : 1) * nsplit);
   const int P = s.T * s.K;
+  // row passes: one when the experts' slots come from the routing (SCAN: K
+  // distinct experts per token, at most T rows each); enough for P = T*K
+  // rows on one expert when they come from a caller's permuted layout
+  const int rows_per_pass = kDecodeRows * (s.T <= kDecodeRows ? 1 : s.T <= 2 * kDecodeRows ? 2 : 4);
+  const int passes = topk_idx ? 1 : (P + rows_per_pass - 1) / rows_per_pass;
+  const dim3 grid(s.n * groups * (UP ? 2 : 1) * nsplit, passes);
   const int klen = (Kdim + nsplit - 1) / nsplit;
   // more token rows per lane means more accumulators: fewer waves, so the
   // registers fit without spilling

@@ -77,10 +77,45 @@ constexpr int NA = 3;                         // activation blocks (steps 2u, 2u
 constexpr int NB = 4;                         // weight stages (step s in stage s % 4)
 constexpr int A_DMA = A_BYTES / 1024 / NWAVES;  // 4 activation DMA instructions per wave per block
 constexpr int B_DMA = B_BYTES / 1024 / NWAVES;  // 2 weight DMA instructions per wave per stage
-constexpr int HALF_A = A_DMA / 2;
 
 static_assert(BM == kTileM, "segment granule must equal the row tile");
 static_assert(A_DMA == 4 && B_DMA == 2, "DMA split assumes 4 + 2 instructions per wave");
+
+// Row-tile classes.  A tile of class FMW has FMW 32-row fragments per wave and
+// covers 64 FMW rows: 256 (FMW = 4, the full tile), 128 (2) or 64 (1); group g
+// owns rows [32 FMW g, 32 FMW (g + 1)).  An expert with at most 128 slots (a
+// small batch, or a lightly routed expert) is one tile of 128 or 64 rows: it
+// multiplies 128 or 64 rows, not 256, and moves a half or a quarter of the
+// activation bytes; its weight bytes and the pipeline are those of a full
+// tile.  Larger experts keep full tiles, their last one padded: a tail tile
+// run apart from its expert's full tiles (a launch of its own) fetched the
+// expert's weight panels from HBM a second time instead of sharing them in L2
+// with the full tiles, and made the skewed workload 8% slower.  The class is
+// chosen per tile inside one persistent launch, in the tile order below.  The
+// activation block of a class holds 64 FMW rows of 128 bytes, loaded by
+// AW(FMW) waves, each AR(FMW) rows as AD(FMW) DMA instructions of 8 rows
+// (1 KiB); with FMW = 1 only group 0 loads activations.
+template <int FMW> constexpr int a_waves() { return FMW == 1 ? NWAVES / 2 : NWAVES; }
+template <int FMW> constexpr int a_rows_per_wave() { return 64 * FMW / a_waves<FMW>(); }
+// activation DMA instructions per block for a wave of group G
+template <int FMW, int G> constexpr int a_dma() {
+  return (FMW == 1 && G == 1) ? 0 : a_rows_per_wave<FMW>() / 8;
+}
+// loads one memory phase issues per wave of group G (weights + half an
+// activation block)
+template <int FMW, int G> constexpr int phase_loads() { return B_DMA + a_dma<FMW, G>() / 2; }
+static_assert(a_dma<4, 0>() == A_DMA && a_dma<4, 1>() == A_DMA, "full tiles: 4 per wave");
+static_assert(a_dma<2, 0>() == 2 && a_dma<2, 1>() == 2 && a_dma<1, 0>() == 2, "half, quarter tiles");
+// runtime forms for a tile's class
+__device__ __forceinline__ int a_rows_per_wave_rt(int fmw) { return fmw == 4 ? 32 : 16; }
+
+// Class of the tiles of an expert with c slots (EVEN shapes; the ragged path
+// runs full tiles only).
+template <bool EVEN>
+__device__ __forceinline__ int tile_fmw(int c) {
+  if (!EVEN) return FM;
+  return c <= 64 ? 1 : (c <= 128 ? 2 : 4);
+}
 
 // LDS blocks/stages as distinct objects, so the compiler can tell the DMA into
 // one from the reads of another (160 KiB in total).
@@ -141,7 +176,8 @@ __device__ __forceinline__ bf16x8 lds_read_wfrag(uint8_t* base, uint32_t off) {
 // Expert e's tiles are v in [nu*offset[e]/BM, nu*offset[e+1]/BM), so the
 // expert is the last e whose segment starts at or before v: a binary search
 // over the monotone offsets (empty experts share their start with the next
-// one, and the last of equal starts is the non-empty segment).
+// one, and the last of equal starts is the non-empty segment).  mt is the
+// tile's row tile within its expert.
 constexpr int kRowBlock = 8;  // row tiles per block of the tile order
 
 __device__ __forceinline__ void decode_tile(int v, const int32_t* __restrict__ offset, int n,
@@ -155,7 +191,7 @@ __device__ __forceinline__ void decode_tile(int v, const int32_t* __restrict__ o
   const int me = offset[lo + 1] / BM - m0;
   const int vl = v - m0 * nu;
   if (me < 2 * kRowBlock) {  // one block
-    mt = m0 + vl % me;
+    mt = vl % me;
     unit = vl / me;
     expert = lo;
     return;
@@ -170,7 +206,7 @@ __device__ __forceinline__ void decode_tile(int v, const int32_t* __restrict__ o
   const int start = b * q + min(b, r);
   const int size = q + (b < r ? 1 : 0);
   const int w = vl - nu * start;
-  mt = m0 + start + w % size;
+  mt = start + w % size;
   unit = w / size;
   expert = lo;
 }
@@ -241,32 +277,36 @@ __device__ __forceinline__ void issue_b(const TileCtx& c, uint8_t* st, int k0) {
   }
 }
 
-// Matrix-core operands of one 16-deep slice: 4 activation fragments (rows) and
-// 2 weight fragments (columns).
+// Matrix-core operands of one 16-deep slice: FMW activation fragments (rows)
+// and 2 weight fragments (columns).
+template <int FMW>
 struct Frags {
-  bf16x8 x[FM], w[FN];
+  bf16x8 x[FMW], w[FN];
 };
 
 // Slice q (0..3) of an activation block and slice kk (0..1) of a weight stage.
+template <int FMW>
 __device__ __forceinline__ void read_frags(const TileCtx& c, uint8_t* blk, uint8_t* st, int q,
-                                           int kk, Frags& f) {
+                                           int kk, Frags<FMW>& f) {
 #pragma unroll
   for (int j = 0; j < FN; ++j) f.w[j] = lds_read_wfrag(st, c.w_rd[j] + kk * 16 * SUBN * 2);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) f.x[i] = lds_read128(blk, c.x_rd[q] + i * 32 * A_ROW);
+  for (int i = 0; i < FMW; ++i) f.x[i] = lds_read128(blk, c.x_rd[q] + i * 32 * A_ROW);
 }
 
-__device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[FM][FN]) {
+template <int FMW>
+__device__ __forceinline__ void mma(const Frags<FMW>& f, f32x16 (&acc)[FM][FN]) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FMW; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[j], f.x[i], acc[i][j], 0, 0, 0);
 }
 
-// Compute phase: the 16 products of one step, both slices' fragments read
+// Compute phase: the 8 FMW products of one step, both slices' fragments read
 // before (in the memory phase), so the matrix core runs them back to back.
-__device__ __forceinline__ void compute_phase(const Frags& f0, const Frags& f1,
+template <int FMW>
+__device__ __forceinline__ void compute_phase(const Frags<FMW>& f0, const Frags<FMW>& f1,
                                               f32x16 (&acc)[FM][FN]) {
   __builtin_amdgcn_s_setprio(1);
   mma(f0, acc);
@@ -274,28 +314,30 @@ __device__ __forceinline__ void compute_phase(const Frags& f0, const Frags& f1,
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Memory phase for step s (S = s % 12):
+// Memory phase for step s (S = s % 12), wave group G:
 //  - read both slices of step R (s for group 1, s + 1 for group 0) into f0, f1;
-//  - issue the weights of step s + 3 and half of the activation block of
-//    steps s + 4, s + 5 (even s) or s + 3, s + 4 (odd s).
+//  - issue the weights of step s + 3 and half of this wave's share of the
+//    activation block of steps s + 4, s + 5 (even s) or s + 3, s + 4 (odd s).
 // The reads are placed ahead of the DMA issue (which blocks the wave) so they
 // complete meanwhile.  Offsets past the end are clamped to the last step or
 // block: those loads land in stages nobody reads, and keep the count of loads
-// in flight the same on every step.
-template <bool EVEN, bool WNT, int S, int R>
-__device__ __forceinline__ void memory_phase(const TileCtx& c, int s, Frags& f0, Frags& f1) {
+// in flight the same on every step (phase_loads<FMW, G>).
+template <bool EVEN, bool WNT, int FMW, int G, int S, int R>
+__device__ __forceinline__ void memory_phase(const TileCtx& c, int s, Frags<FMW>& f0,
+                                             Frags<FMW>& f1) {
   constexpr int RB = R % NB, RA = (R / 2) % NA, RH = R & 1;
   constexpr int SB = (S + 3) % NB;            // stage of step s + 3
   constexpr int SA = (S / 2 + 2) % NA;        // block of steps 2(u+2), 2(u+2)+1, u = s / 2
+  constexpr int AD = a_dma<FMW, G>(), HALF = AD / 2;
   __builtin_amdgcn_s_setprio(0);
-  read_frags(c, a_block<RA>(), b_stage<RB>(), 2 * RH, 0, f0);
-  read_frags(c, a_block<RA>(), b_stage<RB>(), 2 * RH + 1, 1, f1);
+  read_frags<FMW>(c, a_block<RA>(), b_stage<RB>(), 2 * RH, 0, f0);
+  read_frags<FMW>(c, a_block<RA>(), b_stage<RB>(), 2 * RH + 1, 1, f1);
   __builtin_amdgcn_sched_barrier(0);
   issue_b<EVEN, WNT>(c, b_stage<SB>(), min((s + 3) * BK, c.klast_b));
   if constexpr ((S & 1) == 0)
-    issue_a<EVEN, WNT, 0, HALF_A>(c, a_block<SA>(), min((s + 4) * BK, c.klast_a));
+    issue_a<EVEN, WNT, 0, HALF>(c, a_block<SA>(), min((s + 4) * BK, c.klast_a));
   else
-    issue_a<EVEN, WNT, HALF_A, A_DMA>(c, a_block<SA>(), min((s + 3) * BK, c.klast_a));
+    issue_a<EVEN, WNT, HALF, AD>(c, a_block<SA>(), min((s + 3) * BK, c.klast_a));
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -303,44 +345,47 @@ __device__ __forceinline__ void memory_phase(const TileCtx& c, int s, Frags& f0,
 //   group 0: compute(s) | wait | barrier | memory(read s+1) | barrier
 //   group 1: memory(read s) | wait | barrier | compute(s) | barrier
 // The wait at the end of the first phase makes this wave's loads of step s+1
-// complete.  Every memory phase issues 4 loads, counted in issue order, and
-// the last ones step s+1 needs were issued in memory phase s-2, so group 0
-// (last memory phase s-1) may leave 4 in flight and group 1 (last memory
-// phase s) 8.  After the barrier, step s+1 is visible to every wave.
-template <bool EVEN, bool WNT, int G, int S>
-__device__ __forceinline__ void step(const TileCtx& c, int s, Frags& f0, Frags& f1,
+// complete.  Every memory phase of a wave issues L = phase_loads<FMW, G>
+// loads (4 in a full tile), counted in issue order, and the last ones step
+// s+1 needs were issued in memory phase s-2, so group 0 (last memory phase
+// s-1) may leave L in flight and group 1 (last memory phase s) 2 L.  After
+// the barrier, step s+1 is visible to every wave.
+template <bool EVEN, bool WNT, int FMW, int G, int S>
+__device__ __forceinline__ void step(const TileCtx& c, int s, Frags<FMW>& f0, Frags<FMW>& f1,
                                      f32x16 (&acc)[FM][FN]) {
+  constexpr int L = phase_loads<FMW, G>();
   if constexpr (G == 0) {
     compute_phase(f0, f1, acc);
-    wait_vmcnt<4>();
+    wait_vmcnt<L>();
     stage_barrier();
-    memory_phase<EVEN, WNT, S, S + 1>(c, s, f0, f1);
+    memory_phase<EVEN, WNT, FMW, G, S, S + 1>(c, s, f0, f1);
     stage_barrier();
   } else {
-    memory_phase<EVEN, WNT, S, S>(c, s, f0, f1);
-    wait_vmcnt<8>();
+    memory_phase<EVEN, WNT, FMW, G, S, S>(c, s, f0, f1);
+    wait_vmcnt<2 * L>();
     stage_barrier();
     compute_phase(f0, f1, acc);
     stage_barrier();
   }
 }
 
-template <bool EVEN, bool WNT, int G, int I>
-__device__ __forceinline__ void tail_step(const TileCtx& c, int s0, int r, Frags& f0, Frags& f1,
-                                          f32x16 (&acc)[FM][FN]) {
-  if (r > I) step<EVEN, WNT, G, I>(c, s0 + I, f0, f1, acc);
+template <bool EVEN, bool WNT, int FMW, int G, int I>
+__device__ __forceinline__ void tail_step(const TileCtx& c, int s0, int r, Frags<FMW>& f0,
+                                          Frags<FMW>& f1, f32x16 (&acc)[FM][FN]) {
+  if (r > I) step<EVEN, WNT, FMW, G, I>(c, s0 + I, f0, f1, acc);
 }
 
 // Prologue of the ping-pong: every wave issues its share of weight steps 0..2
 // and activation blocks 0, 1 (steps 0..3); memory phase s then issues step
 // s + 3 onwards.  The LDS must be free (every wave past its last reads).
-template <bool EVEN, bool WNT>
+template <bool EVEN, bool WNT, int FMW, int G>
 __device__ __forceinline__ void pp_prologue(const TileCtx& c) {
+  constexpr int AD = a_dma<FMW, G>();
   issue_b<EVEN, WNT>(c, b_stage<0>(), 0);
-  issue_a<EVEN, WNT, 0, A_DMA>(c, a_block<0>(), 0);
+  issue_a<EVEN, WNT, 0, AD>(c, a_block<0>(), 0);
   issue_b<EVEN, WNT>(c, b_stage<1>(), BK);
   issue_b<EVEN, WNT>(c, b_stage<2>(), 2 * BK);
-  issue_a<EVEN, WNT, 0, A_DMA>(c, a_block<1>(), min(2 * BK, c.klast_a));
+  issue_a<EVEN, WNT, 0, AD>(c, a_block<1>(), min(2 * BK, c.klast_a));
 }
 
 // Main loop over the contraction (ksteps even, >= 4 steps of 32), after
@@ -348,59 +393,61 @@ __device__ __forceinline__ void pp_prologue(const TileCtx& c) {
 // order; LOADS_AFTER more loads were issued after the prologue's.  Stores may
 // also be pending; they only make the count stricter, so the wait below holds
 // whatever their order relative to the loads.
-template <bool EVEN, bool WNT, int G, int LOADS_AFTER>
+template <bool EVEN, bool WNT, int FMW, int G, int LOADS_AFTER>
 __device__ __forceinline__ void run_tile_pp_main(const TileCtx& c, int ksteps,
                                                  f32x16 (&acc)[FM][FN]) {
-  // weight step 0 and activation block 0 (the prologue's first 6 loads) landed
-  wait_vmcnt<2 * B_DMA + A_DMA + LOADS_AFTER>();
+  // weight step 0 and this wave's share of activation block 0 (the
+  // prologue's first 2 + AD loads) landed
+  wait_vmcnt<2 * B_DMA + a_dma<FMW, G>() + LOADS_AFTER>();
   stage_barrier();
-  Frags f0, f1;
+  Frags<FMW> f0, f1;
   if (G == 0) {
-    read_frags(c, a_block<0>(), b_stage<0>(), 0, 0, f0);
-    read_frags(c, a_block<0>(), b_stage<0>(), 1, 1, f1);
+    read_frags<FMW>(c, a_block<0>(), b_stage<0>(), 0, 0, f0);
+    read_frags<FMW>(c, a_block<0>(), b_stage<0>(), 1, 1, f1);
   }
   int s = 0;
   for (; s + 12 <= ksteps; s += 12) {
-    step<EVEN, WNT, G, 0>(c, s + 0, f0, f1, acc);
-    step<EVEN, WNT, G, 1>(c, s + 1, f0, f1, acc);
-    step<EVEN, WNT, G, 2>(c, s + 2, f0, f1, acc);
-    step<EVEN, WNT, G, 3>(c, s + 3, f0, f1, acc);
-    step<EVEN, WNT, G, 4>(c, s + 4, f0, f1, acc);
-    step<EVEN, WNT, G, 5>(c, s + 5, f0, f1, acc);
-    step<EVEN, WNT, G, 6>(c, s + 6, f0, f1, acc);
-    step<EVEN, WNT, G, 7>(c, s + 7, f0, f1, acc);
-    step<EVEN, WNT, G, 8>(c, s + 8, f0, f1, acc);
-    step<EVEN, WNT, G, 9>(c, s + 9, f0, f1, acc);
-    step<EVEN, WNT, G, 10>(c, s + 10, f0, f1, acc);
-    step<EVEN, WNT, G, 11>(c, s + 11, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 0>(c, s + 0, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 1>(c, s + 1, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 2>(c, s + 2, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 3>(c, s + 3, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 4>(c, s + 4, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 5>(c, s + 5, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 6>(c, s + 6, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 7>(c, s + 7, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 8>(c, s + 8, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 9>(c, s + 9, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 10>(c, s + 10, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 11>(c, s + 11, f0, f1, acc);
   }
   // 0..11 remaining steps; s is a multiple of 12, so their stage and block
   // indices are those of steps 0..10
   const int r = ksteps - s;
-  tail_step<EVEN, WNT, G, 0>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 1>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 2>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 3>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 4>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 5>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 6>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 7>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 8>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 9>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, G, 10>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 0>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 1>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 2>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 3>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 4>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 5>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 6>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 7>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 8>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 9>(c, s, r, f0, f1, acc);
+  tail_step<EVEN, WNT, FMW, G, 10>(c, s, r, f0, f1, acc);
   // the surplus loads must land before the workgroup's LDS is released
   wait_vmcnt<0>();
 }
 
-template <bool EVEN, bool WNT, int G>
-__device__ __forceinline__ void run_tile_pp(const TileCtx& c, int ksteps, f32x16 (&acc)[FM][FN]) {
-  pp_prologue<EVEN, WNT>(c);
-  run_tile_pp_main<EVEN, WNT, G, 0>(c, ksteps, acc);
+template <bool EVEN, bool WNT, int FMW, int G>
+__device__ __forceinline__ void run_tile_pp(const TileCtx& c, int ksteps,
+                                            f32x16 (&acc)[FM][FN]) {
+  pp_prologue<EVEN, WNT, FMW, G>(c);
+  run_tile_pp_main<EVEN, WNT, FMW, G, 0>(c, ksteps, acc);
 }
 
-// Any number of steps (ragged shapes): one activation block and one weight
-// stage per step pair, every wave loads and computes in the same phase, full
-// waits.
+// Any number of steps (ragged shapes, full tiles only): one activation block
+// and one weight stage per step pair, every wave loads and computes in the
+// same phase, full waits.
 template <bool EVEN, bool WNT>
 __device__ __forceinline__ void run_tile_simple(const TileCtx& c, int ksteps, f32x16 (&acc)[FM][FN]) {
   for (int s = 0; s < ksteps; s += 2) {
@@ -409,14 +456,14 @@ __device__ __forceinline__ void run_tile_simple(const TileCtx& c, int ksteps, f3
     if (s + 1 < ksteps) issue_b<EVEN, WNT>(c, b_stage<1>(), (s + 1) * BK);
     wait_vmcnt<0>();
     stage_barrier();
-    Frags f0, f1;
-    read_frags(c, a_block<0>(), b_stage<0>(), 0, 0, f0);
-    read_frags(c, a_block<0>(), b_stage<0>(), 1, 1, f1);
+    Frags<FM> f0, f1;
+    read_frags<FM>(c, a_block<0>(), b_stage<0>(), 0, 0, f0);
+    read_frags<FM>(c, a_block<0>(), b_stage<0>(), 1, 1, f1);
     mma(f0, acc);
     mma(f1, acc);
     if (s + 1 < ksteps) {
-      read_frags(c, a_block<0>(), b_stage<1>(), 2, 0, f0);
-      read_frags(c, a_block<0>(), b_stage<1>(), 3, 1, f1);
+      read_frags<FM>(c, a_block<0>(), b_stage<1>(), 2, 0, f0);
+      read_frags<FM>(c, a_block<0>(), b_stage<1>(), 3, 1, f1);
       mma(f0, acc);
       mma(f1, acc);
     }
@@ -425,28 +472,38 @@ __device__ __forceinline__ void run_tile_simple(const TileCtx& c, int ksteps, f3
   }
 }
 
-template <bool EVEN, bool WNT>
+template <bool EVEN, bool WNT, int FMW>
 __device__ __forceinline__ void run_tile(const TileCtx& c, int ksteps, int group,
                                          f32x16 (&acc)[FM][FN]) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FMW; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-  if (!EVEN || ksteps < 4)  // the ping-pong needs at least 4 steps (2 activation blocks)
-    run_tile_simple<EVEN, WNT>(c, ksteps, acc);
-  else if (group == 0)
-    run_tile_pp<EVEN, WNT, 0>(c, ksteps, acc);
-  else
-    run_tile_pp<EVEN, WNT, 1>(c, ksteps, acc);
+  // the ragged path and the smaller row classes never meet: the launchers use
+  // the classes only for EVEN shapes, which have at least the 4 steps (2
+  // activation blocks) the ping-pong needs
+  static_assert(EVEN || FMW == FM, "ragged shapes use full tiles");
+  if constexpr (FMW == FM) {
+    if (!EVEN || ksteps < 4) {
+      run_tile_simple<EVEN, WNT>(c, ksteps, acc);
+      return;
+    }
+  }
+  if constexpr (EVEN) {
+    if (group == 0)
+      run_tile_pp<EVEN, WNT, FMW, 0>(c, ksteps, acc);
+    else
+      run_tile_pp<EVEN, WNT, FMW, 1>(c, ksteps, acc);
+  }
 }
 
 // Lane-dependent LDS read offsets shared by both kernels.
-//   wm: 128-row half of the tile; sub[j], cb[j]: weight sub-tile and first
-//   column (within it) of fragment j
-__device__ __forceinline__ void setup_reads(TileCtx& c, int lane, int wm, const int (&sub)[FN],
-                                            const int (&cb)[FN]) {
+//   fmw: the tile's class; wm: group (rows 32 fmw wm .. +32 fmw of the tile);
+//   sub[j], cb[j]: weight sub-tile and first column (within it) of fragment j
+__device__ __forceinline__ void setup_reads(TileCtx& c, int lane, int fmw, int wm,
+                                            const int (&sub)[FN], const int (&cb)[FN]) {
   const int l32 = lane & 31, hi = lane >> 5;
-  const int m = wm * 128 + l32;
+  const int m = wm * 32 * fmw + l32;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     c.x_rd[q] = uint32_t(m * A_ROW + (((2 * q + hi) ^ ((m >> 1) & 7)) << 4));
@@ -459,10 +516,17 @@ __device__ __forceinline__ void setup_reads(TileCtx& c, int lane, int wm, const 
   }
 }
 
-// Activation DMA: instruction i of wave w covers rows w*32 + i*8 .. +8; lane
-// l fetches row +l/8 into physical chunk l%8, i.e. logical chunk
-// (l%8) ^ ((row >> 1) & 7) = (l%8) ^ ((4 i + l/16) & 7).
-__device__ __forceinline__ int a_dma_row(int wave, int i, int lane) { return wave * 32 + i * 8 + (lane >> 3); }
+// Activation DMA: instruction i of wave w covers rows w*AR + i*8 .. +8 (AR =
+// a_rows_per_wave: 32 in a full tile, 16 in the smaller classes); lane l
+// fetches row +l/8 into physical chunk l%8, i.e. logical chunk
+// (l%8) ^ ((row >> 1) & 7) = (l%8) ^ ((4 i + l/16) & 7), since AR/2 * w is a
+// multiple of 8.
+__device__ __forceinline__ int a_dma_row(int fmw, int wave, int i, int lane) {
+  static_assert((a_rows_per_wave<4>() / 2) % 8 == 0 && (a_rows_per_wave<2>() / 2) % 8 == 0 &&
+                    (a_rows_per_wave<1>() / 2) % 8 == 0,
+                "swizzle independent of the wave");
+  return wave * a_rows_per_wave_rt(fmw) + i * 8 + (lane >> 3);
+}
 __device__ __forceinline__ int a_dma_chunk(int i, int lane) { return (lane & 7) ^ ((i * 4 + (lane >> 4)) & 7); }
 
 // Weight DMA: waves 0-3 fill sub-tile 0, waves 4-7 sub-tile 1; wave w fills
@@ -482,27 +546,65 @@ __device__ __forceinline__ void set_klast(TileCtx& c, int ksteps) {
   c.klast_a = ((ksteps - 1) & ~1) * BK;
 }
 
+// The first wait of a tile's main loop allows 4 + AD + LOADS_AFTER loads in
+// flight (see run_tile_pp_main); the per-tile class makes the count a runtime
+// value here, dispatched to the immediate each case needs.
+template <bool EVEN, bool WNT, int G, int LOADS_AFTER>
+__device__ __forceinline__ void run_class(const TileCtx& c, int fmw, int ksteps,
+                                          f32x16 (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+  if (fmw == 4)
+    run_tile_pp_main<EVEN, WNT, 4, G, LOADS_AFTER>(c, ksteps, acc);
+  else if (fmw == 2)
+    run_tile_pp_main<EVEN, WNT, 2, G, LOADS_AFTER>(c, ksteps, acc);
+  else
+    run_tile_pp_main<EVEN, WNT, 1, G, LOADS_AFTER>(c, ksteps, acc);
+}
+
+template <bool EVEN, bool WNT, int G>
+__device__ __forceinline__ void prologue_class(const TileCtx& c, int fmw) {
+  if (fmw == 4)
+    pp_prologue<EVEN, WNT, 4, G>(c);
+  else if (fmw == 2)
+    pp_prologue<EVEN, WNT, 2, G>(c);
+  else
+    pp_prologue<EVEN, WNT, 1, G>(c);
+}
+
 // ---------------------------------------------------------------------------
 // up: h = silu(x w1) * (x w3)
 // ---------------------------------------------------------------------------
-template <bool EVEN, bool WNT, bool KPOW2>
-__global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ expert_offset,
-    const int32_t* __restrict__ row_slot, const uint16_t* __restrict__ w1,
-    const uint16_t* __restrict__ w3, uint16_t* __restrict__ h, int T, int D, int H, int n, int K,
-    int k_shift) {
+// The persistent loop of one wave of group G.
+template <bool EVEN, bool WNT, bool KPOW2, int G>
+__device__ __forceinline__ void up_tiles(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ expert_count,
+    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ row_slot,
+    const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3, uint16_t* __restrict__ h,
+    int T, int D, int H, int n, int K, int k_shift) {
   const int nt_count = (H + SUBN - 1) / SUBN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // wave (wm, wn): rows wm*128 .. +128, columns wn*32 .. +32 of both w1
-  // (fragment 0) and w3 (fragment 1)
-  const int wm = wave >> 2, wn = wave & 3;
+  // wave (wm = G, wn): rows 32 fmw wm .. +32 fmw, columns wn*32 .. +32 of
+  // both w1 (fragment 0) and w3 (fragment 1)
+  const int wm = G, wn = wave & 3;
   const int sub[FN] = {0, 1};
   const int cb[FN] = {wn * 32, wn * 32};
   const int ksteps = (D + BK - 1) / BK;
   const size_t wsz = size_t(D) * H;
 
-  auto make_ctx = [&](int nt_, int e_, const int (&sl)[A_DMA]) {
+  // Row slots of a tile's activation rows: A_DMA per wave for every class
+  // (the rows of the instructions a smaller class does not issue are other
+  // rows of the expert's segment, in range and unused), so that the main
+  // loop's first wait counts the same loads whatever the next tile's class.
+  auto load_slots = [&](int (&sl)[A_DMA], int row0, int fmw) {
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) sl[i] = row_slot[row0 + a_dma_row(fmw, wave, i, lane)];
+  };
+
+  auto make_ctx = [&](int nt_, int e_, int fmw, const int (&sl)[A_DMA]) {
     TileCtx c;
     c.kbase = 0;
     c.ra = make_rsrc(x, uint32_t(T) * D * 2);
@@ -514,44 +616,46 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
       const uint32_t off = tok * uint32_t(D) * 2 + a_dma_chunk(i, lane) * 16;
       c.a_voff[i] = sl[i] >= 0 ? off : kOOB;
     }
-    c.a_dst = wave * 32 * A_ROW;
+    c.a_dst = wave * a_rows_per_wave_rt(fmw) * A_ROW;
     setup_b_dma(c, lane, wave, nt_ * SUBN, H);
-    setup_reads(c, lane, wm, sub, cb);
+    setup_reads(c, lane, fmw, wm, sub, cb);
     set_klast(c, ksteps);
     return c;
   };
 
-  // Epilogue: lane holds token row (wm*128 + 32 i + lane%32) and, per register
-  // quad q, 4 consecutive columns starting at 8 q + 4 (lane/32).  Lanes l and
-  // l+32 hold the two halves of the same 8 columns; they swap one half so that
-  // the lower lane writes quads 0 and 2 and the upper lane quads 1 and 3, each
-  // as one 16-byte store.
-  auto store_h = [&](const f32x16 (&acc)[FM][FN], int row0, int n0) {
-    const int l32 = lane & 31, hi = lane >> 5;
+  // Epilogue: lane holds token row (32 FMW wm + 32 i + lane%32) and, per
+  // register quad q, 4 consecutive columns starting at 8 q + 4 (lane/32).
+  // Lanes l and l+32 hold the two halves of the same 8 columns; they swap one
+  // half so that the lower lane writes quads 0 and 2 and the upper lane quads
+  // 1 and 3, each as one 16-byte store.
+  auto store_rows = [&](const f32x16 (&acc)[FM][FN], int i, int m, int n0) {
+    const int hi = lane >> 5;
+    uint16_t* hrow = h + size_t(m) * H;
+    uint2 pk[4];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = row0 + wm * 128 + i * 32 + l32;
-      uint16_t* hrow = h + size_t(m) * H;
-      uint2 pk[4];
+    for (int q = 0; q < 4; ++q) {
+      float v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = silu(acc[i][0][q * 4 + r]) * acc[i][1][q * 4 + r];
-        pk[q].x = pack_bf16x2(v[0], v[1]);
-        pk[q].y = pack_bf16x2(v[2], v[3]);
-      }
-#pragma unroll
-      for (int qq = 0; qq < 4; qq += 2) {
-        const uint2 send = hi ? pk[qq] : pk[qq + 1];
-        const uint2 mine = hi ? pk[qq + 1] : pk[qq];
-        const uint32_t rx = __shfl_xor(send.x, 32, 64), ry = __shfl_xor(send.y, 32, 64);
-        const int col = n0 + wn * 32 + (qq + hi) * 8;
-        if (!EVEN && col >= H) continue;  // H is a multiple of 8: all 8 columns or none
-        *reinterpret_cast<uint4*>(hrow + col) =
-            hi ? make_uint4(rx, ry, mine.x, mine.y) : make_uint4(mine.x, mine.y, rx, ry);
-      }
+      for (int r = 0; r < 4; ++r) v[r] = silu(acc[i][0][q * 4 + r]) * acc[i][1][q * 4 + r];
+      pk[q].x = pack_bf16x2(v[0], v[1]);
+      pk[q].y = pack_bf16x2(v[2], v[3]);
     }
+#pragma unroll
+    for (int qq = 0; qq < 4; qq += 2) {
+      const uint2 send = hi ? pk[qq] : pk[qq + 1];
+      const uint2 mine = hi ? pk[qq + 1] : pk[qq];
+      const uint32_t rx = __shfl_xor(send.x, 32, 64), ry = __shfl_xor(send.y, 32, 64);
+      const int col = n0 + wn * 32 + (qq + hi) * 8;
+      if (!EVEN && col >= H) continue;  // H is a multiple of 8: all 8 columns or none
+      *reinterpret_cast<uint4*>(hrow + col) =
+          hi ? make_uint4(rx, ry, mine.x, mine.y) : make_uint4(mine.x, mine.y, rx, ry);
+    }
+  };
+  auto store_h = [&](const f32x16 (&acc)[FM][FN], int row0, int n0, int fmw) {
+    const int l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      if (i < fmw) store_rows(acc, i, row0 + wm * 32 * fmw + i * 32 + l32, n0);
   };
 
   // Persistent: one workgroup per compute unit walks tiles L, L + G, ... (G a
@@ -566,94 +670,106 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
   int L = blockIdx.x;
   int mt, nt, e;
   if (!map_tile(L, expert_offset, n, nt_count, mt, nt, e)) return;
+  int fmw = tile_fmw<EVEN>(expert_count[e]);
+  int row0 = expert_offset[e] + mt * BM;
   int slot[A_DMA];
-#pragma unroll
-  for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt * BM + a_dma_row(wave, i, lane)];
-  TileCtx c = make_ctx(nt, e, slot);
-  if constexpr (EVEN) pp_prologue<true, WNT>(c);
+  load_slots(slot, row0, fmw);
+  TileCtx c = make_ctx(nt, e, fmw, slot);
+  if constexpr (EVEN) prologue_class<true, WNT, G>(c, fmw);
   for (;;) {
     int mt2 = 0, nt2 = 0, e2 = 0;
     const bool more = map_tile(L + gridDim.x, expert_offset, n, nt_count, mt2, nt2, e2);
-    const int mt_load = more ? mt2 : mt;  // a valid tile when there is no next one
+    // a valid tile when there is no next one
+    const int fmw2 = more ? tile_fmw<EVEN>(expert_count[e2]) : fmw;
+    const int row0_next = more ? expert_offset[e2] + mt2 * BM : row0;
     asm volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) slot[i] = row_slot[mt_load * BM + a_dma_row(wave, i, lane)];
+    load_slots(slot, row0_next, fmw2);
     asm volatile("" ::: "memory");
 
     f32x16 acc[FM][FN];
     if constexpr (EVEN) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-      if (wm == 0)
-        run_tile_pp_main<true, WNT, 0, A_DMA>(c, ksteps, acc);
-      else
-        run_tile_pp_main<true, WNT, 1, A_DMA>(c, ksteps, acc);
+      run_class<true, WNT, G, A_DMA>(c, fmw, ksteps, acc);
     } else {
-      run_tile<EVEN, WNT>(c, ksteps, wm, acc);
+      run_tile<EVEN, WNT, FM>(c, ksteps, G, acc);
     }
     stage_barrier();  // every wave is past this tile's LDS use
-    const int row0 = mt * BM, n0 = nt * SUBN;
+    const int n0 = nt * SUBN;
     if (more) {
-      c = make_ctx(nt2, e2, slot);
+      c = make_ctx(nt2, e2, fmw2, slot);
       asm volatile("" ::: "memory");
-      if constexpr (EVEN) pp_prologue<true, WNT>(c);
+      if constexpr (EVEN) prologue_class<true, WNT, G>(c, fmw2);
       asm volatile("" ::: "memory");
     }
-    store_h(acc, row0, n0);
+    store_h(acc, row0, n0, fmw);
     if (!more) return;
     L += gridDim.x;
-    mt = mt2;
+    row0 = row0_next;
     nt = nt2;
-    e = e2;
+    fmw = fmw2;
   }
+}
+
+template <bool EVEN, bool WNT, bool KPOW2>
+__global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ expert_count,
+    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ row_slot,
+    const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3, uint16_t* __restrict__ h,
+    int T, int D, int H, int n, int K, int k_shift) {
+  // the wave's group is fixed for the whole launch: waves 0-3 own the first
+  // half of every tile's rows, waves 4-7 the rest
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+    up_tiles<EVEN, WNT, KPOW2, 0>(x, expert_count, expert_offset, row_slot, w1, w3, h, T, D, H, n,
+                                  K, k_shift);
+  else
+    up_tiles<EVEN, WNT, KPOW2, 1>(x, expert_count, expert_offset, row_slot, w1, w3, h, T, D, H, n,
+                                  K, k_shift);
 }
 
 // ---------------------------------------------------------------------------
 // down: y = h w2
 // ---------------------------------------------------------------------------
-// One tile: row tile mt of expert e, 256 output columns from n0, over
-// the contraction range [kbase, kbase + 32 * ksteps), stored to y for the
-// rows that hold slots (rows past the expert's slots are padding: nothing
-// reads them, so they are not written).
-template <bool EVEN, bool WNT>
+// One tile of class FMW for wave group G: 64 FMW rows from row0 of expert e,
+// 256 output columns from n0, over the contraction range [kbase, kbase + 32 *
+// ksteps), stored to y for the rows that hold slots (rows past the expert's
+// slots are padding: nothing reads them, so they are not written).
+template <bool EVEN, bool WNT, int FMW, int G>
 __device__ __forceinline__ void down_tile(const int32_t* __restrict__ expert_count,
                                           const int32_t* __restrict__ expert_offset,
                                           const uint16_t* __restrict__ h,
                                           const uint16_t* __restrict__ w2, float* y,
-                                          int D, int H, int mt, int n0, int e, int kbase,
+                                          int D, int H, int row0, int n0, int e, int kbase,
                                           int ksteps) {
-  const int row0 = mt * BM;
+  constexpr int AD = a_dma<FMW, G>();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   TileCtx c;
   c.kbase = kbase;
-  c.ra = make_rsrc(h + size_t(row0) * H, uint32_t(BM) * H * 2);
+  c.ra = make_rsrc(h + size_t(row0) * H, uint32_t(64 * FMW) * H * 2);
   const size_t wsz = size_t(H) * D;
   c.rb = make_rsrc(w2 + size_t(e) * wsz, uint32_t(wsz * 2));
 #pragma unroll
-  for (int i = 0; i < A_DMA; ++i)
-    c.a_voff[i] = uint32_t(a_dma_row(wave, i, lane)) * uint32_t(H) * 2 + a_dma_chunk(i, lane) * 16;
-  c.a_dst = wave * 32 * A_ROW;
+  for (int i = 0; i < AD; ++i)
+    c.a_voff[i] = uint32_t(a_dma_row(FMW, wave, i, lane)) * uint32_t(H) * 2 +
+                  a_dma_chunk(i, lane) * 16;
+  c.a_dst = wave * a_rows_per_wave<FMW>() * A_ROW;
   setup_b_dma(c, lane, wave, n0 + b_sub_of_wave(wave) * SUBN, D);
-  // wave (wm, wn): rows wm*128 .. +128, columns wn*64 .. +64 of the 256-column
-  // tile (sub-tile wn/2)
-  const int wm = wave >> 2, wn = wave & 3;
+  // wave (wm = G, wn): rows 32 FMW wm .. +32 FMW, columns wn*64 .. +64 of the
+  // 256-column tile (sub-tile wn/2)
+  const int wm = G, wn = wave & 3;
   const int sub[FN] = {wn >> 1, wn >> 1};
   const int cb[FN] = {(wn & 1) * 64, (wn & 1) * 64 + 32};
-  setup_reads(c, lane, wm, sub, cb);
+  setup_reads(c, lane, FMW, wm, sub, cb);
 
   f32x16 acc[FM][FN];
   set_klast(c, ksteps);
-  run_tile<EVEN, WNT>(c, ksteps, wm, acc);
+  run_tile<EVEN, WNT, FMW>(c, ksteps, wm, acc);
 
   const int rend = expert_offset[e] + expert_count[e];
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = row0 + wm * 128 + i * 32 + l32;
+  for (int i = 0; i < FMW; ++i) {
+    const int m = row0 + wm * 32 * FMW + i * 32 + l32;
     if (m >= rend) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -672,8 +788,8 @@ __device__ __forceinline__ void down_tile(const int32_t* __restrict__ expert_cou
 // The contraction (H) can be split into `nsplit` (1 or 2) ranges of `klen`
 // elements; range 0 writes its partial product to y and range 1 to y_part
 // (which may lie in another allocation), and the consumer adds the two.
-template <bool EVEN, bool WNT>
-__global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
+template <bool EVEN, bool WNT, int G>
+__device__ __forceinline__ void down_tiles(
     const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2, float* __restrict__ y,
     int D, int H, int n, int nsplit, int klen, float* __restrict__ y_part) {
@@ -695,8 +811,20 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
     const int nt = unit - ks * nt_count;
     const int kbase = ks * klen;
     const int ksteps = (min(klen, H - kbase) + BK - 1) / BK;
-    down_tile<EVEN, WNT>(expert_count, expert_offset, h, w2, ks == 0 ? y : y_part, D, H, mt,
-                         nt * 2 * SUBN, e, kbase, ksteps);
+    const int row0 = expert_offset[e] + mt * BM;
+    float* out = ks == 0 ? y : y_part;
+    const int fmw = tile_fmw<EVEN>(expert_count[e]);
+    if (fmw == 4 || !EVEN)
+      down_tile<EVEN, WNT, FM, G>(expert_count, expert_offset, h, w2, out, D, H, row0,
+                                  nt * 2 * SUBN, e, kbase, ksteps);
+    else if constexpr (EVEN) {
+      if (fmw == 2)
+        down_tile<EVEN, WNT, 2, G>(expert_count, expert_offset, h, w2, out, D, H, row0,
+                                   nt * 2 * SUBN, e, kbase, ksteps);
+      else
+        down_tile<EVEN, WNT, 1, G>(expert_count, expert_offset, h, w2, out, D, H, row0,
+                                   nt * 2 * SUBN, e, kbase, ksteps);
+    }
     stage_barrier();  // every wave is past this tile's LDS use before the next tile's loads
     if (!more) return;
     L += gridDim.x;
@@ -704,6 +832,17 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
     unit = unit2;
     e = e2;
   }
+}
+
+template <bool EVEN, bool WNT>
+__global__ __launch_bounds__(NTHR, 1) void grouped_down_kernel(
+    const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2, float* __restrict__ y,
+    int D, int H, int n, int nsplit, int klen, float* __restrict__ y_part) {
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+    down_tiles<EVEN, WNT, 0>(expert_count, expert_offset, h, w2, y, D, H, n, nsplit, klen, y_part);
+  else
+    down_tiles<EVEN, WNT, 1>(expert_count, expert_offset, h, w2, y, D, H, n, nsplit, klen, y_part);
 }
 
 
@@ -743,9 +882,10 @@ bool weights_streamed(const Shape& s) {
 
 }  // namespace
 
-hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_offset,
-                             const int32_t* row_slot, const uint16_t* w1, const uint16_t* w3,
-                             uint16_t* h, hipStream_t stream) {
+hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
+                             const int32_t* expert_offset, const int32_t* row_slot,
+                             const uint16_t* w1, const uint16_t* w3, uint16_t* h,
+                             hipStream_t stream) {
   const int mt_max = int(s.cap / BM);
   const int nt = (s.H + SUBN - 1) / SUBN;
   if (mt_max * nt == 0) return hipSuccess;
@@ -763,8 +903,8 @@ hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* e
                                   : grouped_up_kernel<false, true, false>)
                           : (pow2 ? grouped_up_kernel<false, false, true>
                                   : grouped_up_kernel<false, false, false>));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), 0, stream, x, expert_offset, row_slot, w1, w3,
-                     h, s.T, s.D, s.H, s.n, s.K, k_shift);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), 0, stream, x, expert_count, expert_offset,
+                     row_slot, w1, w3, h, s.T, s.D, s.H, s.n, s.K, k_shift);
   return hipGetLastError();
 }
 

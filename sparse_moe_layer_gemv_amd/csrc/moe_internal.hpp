@@ -17,9 +17,10 @@ constexpr int kMaxExperts = 256;
 // then holds at most 64 token rows (4 groups of 16 per lane).
 constexpr int kStreamMaxTokens = 64;
 // Largest T for which the automatic path choice streams: the small-batch sweep
-// (Mixtral shape) measures streaming faster up to T = 48 and the tiled path
-// faster from T = 64 on.
-constexpr int kDecodeMaxTokens = 48;
+// (Mixtral shape) measures streaming faster up to T = 32 (488 against 492 us)
+// and the tiled path faster from T = 48 on (494 against 566 us), since
+// experts of at most 128 rows run as 128- or 64-row tiles.
+constexpr int kDecodeMaxTokens = 32;
 // Token rows handled together by one decode pass (one 16x16 MFMA column block).
 constexpr int kDecodeRows = 16;
 
@@ -42,10 +43,13 @@ hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* expe
                           hipStream_t stream);
 
 // Tiled matrix-core path: h = silu(x w1) * (x w3) per expert segment, then
-// y_rows = h w2.  h is bf16 [cap][H] in the workspace.
-hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_offset,
-                             const int32_t* row_slot, const uint16_t* w1, const uint16_t* w3,
-                             uint16_t* h, hipStream_t stream);
+// y_rows = h w2.  h is bf16 [cap][H] in the workspace.  Experts with at most
+// 128 slots run as one tile of 128 or 64 rows (chosen from expert_count on
+// the device), larger ones as full 256-row tiles.
+hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
+                             const int32_t* expert_offset, const int32_t* row_slot,
+                             const uint16_t* w1, const uint16_t* w3, uint16_t* h,
+                             hipStream_t stream);
 // The second product may be split along its contraction into nsplit = 2
 // partial sums (see grouped_down_splits): partial 0 at y_rows, partial 1 at
 // y_part (unused, may be null, when nsplit = 1).

@@ -1,6 +1,6 @@
 """GPU parity of every libmoe entry point against the fp64 oracle, at sizes the
 oracle finishes in seconds: several row/column/contraction tiles, ragged
-tails, both expert paths (weight streaming for T <= 48 by default, up to 64
+tails, both expert paths (weight streaming for T <= 32 by default, up to 64
 when forced; matrix-core tiles above), forced skewed and empty-expert routings, K and n variants."""
 import numpy as np
 import pytest
@@ -55,8 +55,8 @@ SHAPES = [
     ("decode_t16", 16, 512, 1024, 8, 2, 15),
     ("decode_t17", 17, 512, 1024, 8, 2, 16),
     ("decode_t32", 32, 384, 640, 8, 2, 17),
-    ("stream_t33", 33, 512, 1024, 8, 2, 18),
-    ("stream_t48", 48, 512, 1024, 8, 2, 26),
+    ("tiled_t33", 33, 512, 1024, 8, 2, 18),
+    ("tiled_t48", 48, 512, 1024, 8, 2, 26),
     ("tiled_t49", 49, 512, 1024, 8, 2, 27),
     ("k1_switch", 200, 256, 512, 8, 1, 19),
     ("n16_k4", 130, 256, 384, 16, 4, 20),
@@ -227,6 +227,11 @@ FORCED = [
     # two experts of 17 row tiles each: both cut into row blocks of 9 and 8 in
     # the tile order
     ("two_experts_17_row_tiles", lambda T: np.tile([[5, 2]], (T, 1)), 4200, 256, 384),
+    # the tiled products cover an expert's rows with full 256-row tiles and
+    # one tail tile of 64 rows (tail <= 64), 128 rows (<= 128) or 256 rows:
+    # counts on both sides of every class boundary, with the second product's
+    # contraction split in two (H = 1024)
+    ("row_classes", None, 1, 512, 1024),
 ]
 
 
@@ -235,10 +240,22 @@ def _forced_counts_case():
     return np.concatenate([np.zeros(255), np.ones(256), np.full(257, 2)]).astype(np.int32)[:, None]
 
 
+ROW_CLASS_COUNTS = [1, 63, 64, 65, 127, 128, 129, 256 + 64]
+
+
+def _row_class_case():
+    # K = 1, expert e holds ROW_CLASS_COUNTS[e] slots, tokens interleaved
+    idx = np.concatenate([np.full(c, e) for e, c in enumerate(ROW_CLASS_COUNTS)])
+    return np.random.default_rng(7).permutation(idx).astype(np.int32)[:, None]
+
+
 @pytest.mark.parametrize("label,make,T,D,H", FORCED, ids=[f[0] for f in FORCED])
 def test_grouped_ffn_forced_routing(moe, label, make, T, D, H):
     import torch
-    idx = _forced_counts_case() if make is None else np.asarray(make(T), np.int32)
+    if label == "row_classes":
+        idx = _row_class_case()
+    else:
+        idx = _forced_counts_case() if make is None else np.asarray(make(T), np.int32)
     T, K = idx.shape
     n = 8
     L = moe_synth.make_layer(T, D, H, n, K, seed=41)

@@ -43,7 +43,7 @@ def _layer(moe, L, T, fn):
 # split; the forced streaming path at 64 tokens with wide experts (the
 # second product in 4 partials)
 CASES = [
-    ("n8_k2", 40, 7, 1024, 2048, 8, 2, 0),
+    ("n8_k2", 32, 7, 1024, 2048, 8, 2, 0),
     ("n160_k8", 16, 3, 2048, 256, 160, 8, 0),
     ("stream_t64_wide", 64, 33, 512, 4096, 8, 2, 1),
 ]
