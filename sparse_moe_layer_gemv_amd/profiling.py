@@ -261,6 +261,32 @@ def cmd_mfma(a) -> int:
     return 0
 
 
+def cmd_counters(a) -> int:
+    """Any --pmc pass: per-dispatch values and medians of every counter for one
+    kernel, into profiles/<name>.md."""
+    rows = read_counters(a.dir, a.regex)
+    if not rows:
+        raise RuntimeError("no dispatch of the kernel in the counter run")
+    keys = [k for k in next(iter(rows.values())) if k not in ("kernel", "dur_us")]
+    lines = [f"# {a.title}", "",
+             "Command (on the MI355X box, from the repository root; $REPO is the repository path):",
+             "", "```", "cd /tmp && export TMPDIR=/tmp"] + a.command + ["```", "",
+             "| dispatch | kernel | duration (us) | " + " | ".join(keys) + " |",
+             "|---|---|---|" + "---|" * len(keys)]
+    for i, r in rows.items():
+        lines.append(f"| {i} | `{r['kernel']}` | {r['dur_us']:.1f} | " +
+                     " | ".join(f"{r.get(k, 0):.0f}" for k in keys) + " |")
+    steady = list(rows.values())[1:] or list(rows.values())
+    med = {k: statistics.median([r.get(k, 0.0) for r in steady]) for k in keys + ["dur_us"]}
+    lines += ["", "Medians over the dispatches after the first:", "", "```json",
+              json.dumps(med, indent=1), "```", ""] + a.note + [""]
+    out = os.path.join(PROFILES, f"{a.name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+    return 0
+
+
 def cmd_stats(a) -> int:
     with open(a.csv) as f:
         rows = list(csv.DictReader(f))
@@ -302,13 +328,21 @@ def main(argv=None) -> int:
     m.add_argument("--grbm-scale", type=float, default=1.0,
                    help="divide GRBM_GUI_ACTIVE by this (instances summed into the counter)")
     m.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters", help="any --pmc pass of one kernel -> profiles/<name>.md")
+    c.add_argument("--name", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--regex", required=True)
+    c.add_argument("--dir", required=True)
+    c.add_argument("--command", action="append", default=[])
+    c.add_argument("--note", action="append", default=[], help="line of interpretation to append")
     s = sub.add_parser("stats", help="rocprofv3 --stats csv -> markdown")
     s.add_argument("--csv", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
-    return {"copy": cmd_copy, "traffic": cmd_traffic, "mfma": cmd_mfma, "stats": cmd_stats}[a.cmd](a)
+    return {"copy": cmd_copy, "traffic": cmd_traffic, "mfma": cmd_mfma, "counters": cmd_counters,
+            "stats": cmd_stats}[a.cmd](a)
 
 
 if __name__ == "__main__":
