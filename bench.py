@@ -283,14 +283,14 @@ def stages_alone(args, torch, moe):
     return 0
 
 
-def time_workload(name, L, dev, steps, warmup, torch, moe, load_traffic, ev):
+def time_workload(name, L, dev, steps, warmup, torch, moe, load_traffic, ev, tokens=None):
     """Time `steps` layer passes of workload `name` (after `warmup` untimed
     ones) on inputs already in HBM.  dev: the uploaded x, w_gate, w1, w3, w2.
     Returns the per-workload record (time, throughput, stage breakdown and
     the dominant kernel's roofline)."""
     w = moe_synth.WORKLOADS[name]
-    T, D, H, n, K = w.T, w.D, w.H, w.n, w.K
-    chunk = w.chunk or T
+    T, D, H, n, K = (tokens or w.T), w.D, w.H, w.n, w.K
+    chunk = min(w.chunk or T, T)
     x, wg, w1, w3, w2 = dev
     out = torch.empty((T, D), dtype=torch.float32, device="cuda:0")
     idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
@@ -362,7 +362,7 @@ def time_workload(name, L, dev, steps, warmup, torch, moe, load_traffic, ev):
     kernel = "decode_up" if decode else "grouped_up"
     # HBM bytes per launch from the stored counter runs of this exact kernel
     # source (None once the source has changed since they were taken)
-    tr = load_traffic(kernel, name)
+    tr = load_traffic(kernel, name) if tokens in (None, w.T) else None
     traffic = None if tr is None else tr["bytes_per_launch"]
     # The dominant kernel's bound: the larger of its time at the matrix-core
     # peak (algorithmic FLOPs) and at the HBM peak (algorithmic bytes: w1 and
@@ -428,6 +428,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=sorted(moe_synth.WORKLOADS))
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the headline workload with this many tokens (a prefix of its x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true",
                     help="time only the headline workload (no per-workload sub-records)")
@@ -469,7 +471,8 @@ def main(argv=None):
         w = moe_synth.WORKLOADS[name]
         log(f"[bench] generating {name} inputs T={w.T} D={w.D} H={w.H} n={w.n} K={w.K}")
         t0 = time.perf_counter()
-        L = moe_synth.make_workload(name)
+        tok = args.tokens if (name == args.workload and args.tokens) else None
+        L = moe_synth.make_workload(name, T=tok)
         log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
         key = (w.weight_seed, w.D, w.H, w.n)
         if key not in uploaded:
@@ -480,7 +483,7 @@ def main(argv=None):
         steps = args.steps if name == args.workload else side[name]
         warmup = args.warmup if name == args.workload else min(args.warmup, 3)
         records[name] = time_workload(name, L, dev, steps, warmup, torch, moe, load_traffic,
-                                      HipEvents())
+                                      HipEvents(), tokens=tok)
         del dev
         if name == args.workload:
             head_inputs = L
@@ -513,7 +516,7 @@ def main(argv=None):
         rec["workloads"] = {nm: r for nm, r in records.items() if nm != args.workload}
 
     if not args.no_cpu_baseline:
-        T = moe_synth.WORKLOADS[args.workload].T
+        T = args.tokens or moe_synth.WORKLOADS[args.workload].T
         sample = args.cpu_sample or min(T, 4096)
         log(f"[bench] timing the fp64 oracle on {sample} tokens")
         rec["cpu_baseline"] = cpu_baseline(args.workload, head_inputs, sample)

@@ -29,6 +29,8 @@
 // forms its h fragment as bf16(silu(a) * b) while loading it (the same single
 // rounding as the tiled path), and the 14336-deep contraction is split into
 // partial sums written to separate buffers, added in order by the combine.
+#include <algorithm>
+
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -342,16 +344,26 @@ hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const float* ab, c
                                         stream);
 }
 
-// Contraction splits of the first product (narrow experts only), while each
-// wave still gets at least 4 of the 32-deep steps.
+// Workgroups that have work when at most min(n, T*K) experts are touched.
+constexpr int kWantActive = 512;
+int touched_max(const Shape& s) { return std::min(s.n, s.T * s.K); }
+
+// Contraction splits of the first product: narrow experts split in two; wide
+// ones split while too few experts are touched to give the chip kWantActive
+// workgroups, as long as each wave keeps at least 4 of the 32-deep steps.
 int decode_up_splits(const Shape& s) {
-  return up_blocks(s) == 1 && s.D % 64 == 0 && s.D / 2 >= 32 * 4 * kUpWaves ? 2 : 1;
+  if (up_blocks(s) == 1) return s.D % 64 == 0 && s.D / 2 >= 32 * 4 * kUpWaves ? 2 : 1;
+  const int per = ((s.H + 127) / 128 + 1) / 2 * 2;  // workgroups per expert and split
+  int n = 1;
+  while (n < 4 && touched_max(s) * per * n < kWantActive && s.D % (64 * 2 * n) == 0 &&
+         s.D / (2 * n) >= 32 * 4 * (kUpWaves / 2))
+    n *= 2;
+  return n;
 }
 
-// Two column blocks per workgroup in the second product when it reads a
-// single partial of a and b.
+// Two column blocks per workgroup in the second product for wide outputs.
 int down_blocks(const Shape& s) {
-  return decode_up_splits(s) == 1 && (s.D + 127) / 128 >= 2 ? 2 : 1;
+  return (up_blocks(s) == 2 || decode_up_splits(s) == 1) && (s.D + 127) / 128 >= 2 ? 2 : 1;
 }
 
 }  // namespace
@@ -363,11 +375,17 @@ size_t decode_scratch_bytes(const Shape& s) {
 int decode_down_splits(const Shape& s) {
   // Split the contraction while each part still gives every wave of a group at
   // least 4 of the 32-deep steps; with two column blocks per workgroup, twice
-  // as many parts keep the workgroup count.
-  const int wpg = down_blocks(s) == 2 ? kDownWaves / 2 : kDownWaves;
+  // as many parts keep the workgroup count.  When few experts are touched,
+  // split further (up to 8) until kWantActive workgroups have work.
+  const int nb = down_blocks(s);
+  const int wpg = nb == 2 ? kDownWaves / 2 : kDownWaves;
+  const int groups = ((s.D + 127) / 128 + nb - 1) / nb;
   int n = 1;
-  const int want = down_blocks(s) == 2 ? 4 : 2;
+  const int want = nb == 2 ? 4 : 2;
   while (n < want && s.H % (64 * n) == 0 && s.H / (2 * n) >= 32 * 4 * wpg) n *= 2;
+  while (n < 8 && touched_max(s) * groups * n < kWantActive && s.H % (64 * 2 * n) == 0 &&
+         s.H / (2 * n) >= 32 * 4 * wpg / 2)
+    n *= 2;
   return n;
 }
 

@@ -85,6 +85,27 @@ def test_decode_t16(moe, mixtral_weights):
     _run(moe, "decode", mixtral_weights)
 
 
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_decode_few_tokens(moe, mixtral_weights, T):
+    # one to four tokens touch at most 2 to 8 experts: the weight-streaming
+    # kernels split their contractions further to keep the chip busy
+    import torch
+    wg_f32, (w1, w3, w2), d = mixtral_weights
+    w = moe_synth.WORKLOADS["decode"]
+    x = moe_synth.make_x(w.x_seed, T, w.D)
+    wg = moe_synth.bf16_bits(wg_f32)
+    idx = torch.empty((T, 2), dtype=torch.int32, device="cuda:0")
+    gate = torch.empty((T, 2), dtype=torch.float32, device="cuda:0")
+    out = moe.forward(dev_bf16(x), dev_bf16(wg), d["w1"], d["w3"], d["w2"], 2, topk_idx=idx,
+                      topk_gate=gate)
+    rr = parity.check_routing(moe_ref.router_logits(x, wg), 2, host(idx), host(gate))
+    assert rr.ok, rr
+    ref = moe_ref.moe_layer(x, wg, w1, w3, w2, 2, forced_idx=rr.forced_idx)
+    orep = parity.check_output(ref["y"], host(out))
+    print(f"[decode T={T}] max/RMS={orep.max_rel:.3e} mean/RMS={orep.mean_rel:.3e}")
+    assert orep.ok, orep
+
+
 def test_prefill_t4096(moe, mixtral_weights):
     counts = _run(moe, "prefill", mixtral_weights)
     assert np.all(np.abs(counts / counts.sum() - 0.125) < 0.01)
