@@ -206,6 +206,53 @@ def crossover(args, torch, moe):
     return 0
 
 
+def weight_data(args, torch, moe):
+    """The layer at a workload's shape with the same x and router but four
+    kinds of expert weights: the random weights it is benchmarked with, all
+    zero, one constant (2^-7) and random signs of that constant.  Every run does
+    the same work in the same order; only the values the matrix cores multiply
+    differ.  Under the board's power limit the clock follows the switching
+    activity of that data, so the differences in time are the share of the
+    expert products' cost that power, not the kernels' structure, decides."""
+    name = args.workload
+    w = moe_synth.WORKLOADS[name]
+    order = args.weight_data.split(",")
+    unknown = [k for k in order if k not in ("random", "zero", "const", "sign")]
+    if unknown:
+        raise SystemExit(f"--weight-data: unknown kinds {unknown}; known: random, zero, const, sign")
+    log(f"[weight-data] generating {name} inputs")
+    L = moe_synth.make_workload(name)
+    x, wg = to_dev(L.x), to_dev(L.w_gate)
+    rand = tuple(to_dev(a) for a in (L.w1, L.w3, L.w2))
+    const = 2.0 ** -7
+    kinds = {
+        "random": lambda: rand,
+        "zero": lambda: tuple(torch.zeros_like(t) for t in rand),
+        "const": lambda: tuple(torch.full_like(t, const) for t in rand),
+        "sign": lambda: tuple((torch.sign(t.float()) * const).to(torch.bfloat16) for t in rand),
+    }
+    from sparse_moe_layer_gemv_amd.profiling import load_traffic
+    rows = []
+    for kind in order:
+        w1, w3, w2 = kinds[kind]()
+        r = time_workload(name, L, (x, wg, w1, w3, w2), args.steps, args.warmup, torch, moe,
+                          load_traffic, HipEvents())
+        rows.append({"weights": kind, "ms_per_step": r["ms_per_step"],
+                     "step_gpu_ms": r["step_gpu_ms"]["median"],
+                     "mfma_peak_frac": r.get("mfma_peak_frac"),
+                     "stage_us": {k: round(v * 1e3, 1) for k, v in r["stage_ms"].items()}})
+        log(f"[weight-data] {kind}: {r['ms_per_step']:.4f} ms/step")
+        del w1, w3, w2
+    rec = {"metric": "layer time by expert-weight data (same routing and work)", "unit": "ms",
+           "data": "synthetic", "dtype": "bf16",
+           "config": {"workload": name, "tokens": w.T, "dim": w.D, "hidden": w.H,
+                      "n_experts": w.n, "top_k": w.K, "steps": args.steps,
+                      "warmup": args.warmup},
+           "rows": rows}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 ROTATION_BYTES = 1 << 30  # inputs rotated per stage, so that every call reads from HBM
 
 
@@ -438,6 +485,11 @@ def main(argv=None):
     ap.add_argument("--crossover", action="store_true",
                     help="small-batch sweep: time both expert-product paths for T = 1..256 and "
                          "print one JSON line with the measured crossover")
+    ap.add_argument("--weight-data", nargs="?", const="random,zero,const,sign,random,zero",
+                    metavar="KINDS",
+                    help="time the workload with random, zero, constant and random-sign expert "
+                         "weights, in the comma-separated order KINDS (same routing and work; "
+                         "one JSON line)")
     ap.add_argument("--stages", action="store_true",
                     help="router, permute and combine each timed alone at the workload's shape, "
                          "over rotating inputs of at least 1 GiB (one JSON line)")
@@ -457,6 +509,8 @@ def main(argv=None):
         return crossover(args, torch, moe)
     if args.stages:
         return stages_alone(args, torch, moe)
+    if args.weight_data:
+        return weight_data(args, torch, moe)
 
     names = [args.workload]
     side = {}
