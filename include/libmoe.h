@@ -232,10 +232,11 @@ int32_t moe_decode_max_tokens(void);
  * allocates and frees nothing.
  *   Accepted: the batches moe_forward streams (T <= moe_decode_max_tokens()
  *   with path AUTO, T <= 64 with path STREAM) whose intermediates fit the
- *   array: about 4*T*K*(2 + 2*S1*H + S2*D) bytes, S1 = 1 or 2 first-product
- *   partials, S2 = 1..4 second-product partials (Mixtral's shape, D = 4096,
- *   H = 14336, K = 2, needs 23 MB at T = 64).  Other shapes, and path TILED,
- *   return MOE_ENOTSUP with nothing enqueued.
+ *   array: about 4*T*K*(2 + 2*S1*H + S2*D) bytes, S1 = 1, 2 or 4
+ *   first-product partials and S2 = 1..8 second-product partials (the larger
+ *   counts when few experts can be touched, i.e. small T*K).  Mixtral's shape
+ *   (D = 4096, H = 14336, K = 2) needs 23 MB at T = 64.  Other shapes, and
+ *   path TILED, return MOE_ENOTSUP with nothing enqueued.
  *   stream must belong to the calling thread's current device (MOE_EINVAL
  *   otherwise).
  * Every call on one GPU uses that GPU's single array and leaves its contents
