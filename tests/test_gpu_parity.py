@@ -331,14 +331,20 @@ def test_grouped_ffn_leaves_padding_rows(moe, T, D, H, path):
     assert orep.ok, orep
 
 
-def test_forward_is_deterministic_and_bf16_output_is_rne_of_fp32(moe):
+# both expert-product paths: the tiled one combines permuted rows, the
+# streaming one (automatic at 16 tokens, forced at 40) rows indexed by slot
+@pytest.mark.parametrize("T,path", [(1000, 0), (16, 0), (40, 1), (24, 2)],
+                         ids=["tiled", "stream", "stream_forced", "tiled_forced"])
+def test_forward_is_deterministic_and_bf16_output_is_rne_of_fp32(moe, T, path):
     import torch
-    L = moe_synth.make_layer(1000, 512, 768, 8, 2, seed=51)
+    L = moe_synth.make_layer(T, 512, 768, 8, 2, seed=51)
     d = _upload(L)
-    a = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2))
-    b = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2))
+    run = lambda **kw: host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, path=path,
+                                        **kw))
+    a = run()
+    b = run()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    c = host(moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, out_dtype=moe.MOE_BF16))
+    c = run(out_dtype=moe.MOE_BF16)
     assert np.array_equal(c, moe_synth.bf16_bits(a))
 
 

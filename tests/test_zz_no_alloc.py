@@ -66,6 +66,12 @@ def test_noalloc_matches_forward(moe, label, T1, T2, D, H, n, K, path):
         y = moe_ref.moe_layer(L.x[:T], L.w_gate, L.w1, L.w3, L.w2, K, forced_idx=rr.forced_idx)["y"]
         orep = parity.check_output(y, out)
         assert orep.ok, orep
+        # bf16 output: the same fp32 sums, rounded to nearest even
+        import torch
+        ob = torch.empty((T, D), dtype=torch.bfloat16, device="cuda:0")
+        w = [dev_bf16(a) for a in (L.w_gate, L.w1, L.w3, L.w2)]
+        moe.forward_noalloc(dev_bf16(L.x[:T]), *w, K, out=ob, out_dtype=moe.MOE_BF16, path=path)
+        assert np.array_equal(host(ob), moe_synth.bf16_bits(out))
 
 
 def test_noalloc_refuses_what_does_not_fit(moe):
