@@ -254,26 +254,32 @@ struct TileCtx {
 // otherwise it goes into the range-checked vector offset, so weight rows past
 // the contraction end read as zero (and activation columns past it meet those
 // zero rows).
+// past: the step lies beyond the contraction's end (a surplus load of the
+// last steps, issued only to keep the number of loads in flight the same on
+// every step): its offset is out of range, so the hardware returns zeros
+// without a memory access, into a stage no wave reads.
 template <bool EVEN, bool WNT, int I0, int I1>
-__device__ __forceinline__ void issue_a(const TileCtx& c, uint8_t* blk, int k0) {
+__device__ __forceinline__ void issue_a(const TileCtx& c, uint8_t* blk, int k0, bool past = false) {
   const uint32_t kb = uint32_t(c.kbase + k0) * 2;
 #pragma unroll
   for (int i = I0; i < I1; ++i) {
+    const uint32_t voff = past ? kOOB : c.a_voff[i];
     if (EVEN)
-      dma16(c.ra, lds(blk) + c.a_dst + i * 1024, c.a_voff[i], kb);
+      dma16(c.ra, lds(blk) + c.a_dst + i * 1024, voff, kb);
     else
-      dma16(c.ra, lds(blk) + c.a_dst + i * 1024, c.a_voff[i] + kb, 0);
+      dma16(c.ra, lds(blk) + c.a_dst + i * 1024, voff + kb, 0);
   }
 }
 template <bool EVEN, bool WNT>
-__device__ __forceinline__ void issue_b(const TileCtx& c, uint8_t* st, int k0) {
+__device__ __forceinline__ void issue_b(const TileCtx& c, uint8_t* st, int k0, bool past = false) {
+  const uint32_t voff = past ? kOOB : c.b_voff;
 #pragma unroll
   for (int i = 0; i < B_DMA; ++i) {
     const uint32_t rows = uint32_t(c.kbase + k0 + i * 4) * c.b_row_bytes;
     if (EVEN)
-      dma16<WNT>(c.rb, lds(st) + c.b_dst + i * 1024, c.b_voff, rows);
+      dma16<WNT>(c.rb, lds(st) + c.b_dst + i * 1024, voff, rows);
     else
-      dma16<WNT>(c.rb, lds(st) + c.b_dst + i * 1024, c.b_voff + rows, 0);
+      dma16<WNT>(c.rb, lds(st) + c.b_dst + i * 1024, voff + rows, 0);
   }
 }
 
@@ -319,9 +325,12 @@ __device__ __forceinline__ void compute_phase(const Frags<FMW>& f0, const Frags<
 //  - issue the weights of step s + 3 and half of this wave's share of the
 //    activation block of steps s + 4, s + 5 (even s) or s + 3, s + 4 (odd s).
 // The reads are placed ahead of the DMA issue (which blocks the wave) so they
-// complete meanwhile.  Offsets past the end are clamped to the last step or
-// block: those loads land in stages nobody reads, and keep the count of loads
-// in flight the same on every step (phase_loads<FMW, G>).
+// complete meanwhile.  Loads of steps past the end are still issued, so the
+// count of loads in flight is the same on every step (phase_loads<FMW, G>),
+// but with an out-of-range offset: they read no memory and land (as zeros)
+// in stages nobody reads.  Clamped to the last step instead, they fetched it
+// again (from HBM where weights are loaded non-temporally): fine_prefill
+// 0.947-0.950 -> 0.932-0.940 ms per step, prefill unchanged.
 template <bool EVEN, bool WNT, int FMW, int G, int S, int R>
 __device__ __forceinline__ void memory_phase(const TileCtx& c, int s, Frags<FMW>& f0,
                                              Frags<FMW>& f1) {
@@ -333,11 +342,13 @@ __device__ __forceinline__ void memory_phase(const TileCtx& c, int s, Frags<FMW>
   read_frags<FMW>(c, a_block<RA>(), b_stage<RB>(), 2 * RH, 0, f0);
   read_frags<FMW>(c, a_block<RA>(), b_stage<RB>(), 2 * RH + 1, 1, f1);
   __builtin_amdgcn_sched_barrier(0);
-  issue_b<EVEN, WNT>(c, b_stage<SB>(), min((s + 3) * BK, c.klast_b));
+  issue_b<EVEN, WNT>(c, b_stage<SB>(), min((s + 3) * BK, c.klast_b), (s + 3) * BK > c.klast_b);
   if constexpr ((S & 1) == 0)
-    issue_a<EVEN, WNT, 0, HALF>(c, a_block<SA>(), min((s + 4) * BK, c.klast_a));
+    issue_a<EVEN, WNT, 0, HALF>(c, a_block<SA>(), min((s + 4) * BK, c.klast_a),
+                                (s + 4) * BK > c.klast_a);
   else
-    issue_a<EVEN, WNT, HALF, AD>(c, a_block<SA>(), min((s + 3) * BK, c.klast_a));
+    issue_a<EVEN, WNT, HALF, AD>(c, a_block<SA>(), min((s + 3) * BK, c.klast_a),
+                                 (s + 3) * BK > c.klast_a);
   __builtin_amdgcn_sched_barrier(0);
 }
 
