@@ -34,12 +34,12 @@ def fine_weights():
     return moe_synth.bf16_bits(wg_f32), (w1, w3, w2), d
 
 
-def _run(moe, name, fine_weights):
+def _run(moe, name, fine_weights, T=None):
     import torch
     w = moe_synth.WORKLOADS[name]
     wg, (w1, w3, w2), d = fine_weights
-    x = moe_synth.make_x(w.x_seed, w.T, w.D)
-    T, K = w.T, w.K
+    T, K = (T or w.T), w.K
+    x = moe_synth.make_x(w.x_seed, T, w.D)
     out = torch.empty((T, w.D), dtype=torch.float32, device="cuda:0")
     idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
     gate = torch.empty((T, K), dtype=torch.float32, device="cuda:0")
@@ -63,6 +63,14 @@ def _run(moe, name, fine_weights):
 
 def test_fine_decode_t16(moe, fine_weights):
     _run(moe, "fine_decode", fine_weights)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_fine_decode_few_tokens(moe, fine_weights, T):
+    # 8 or 32 of the 160 experts touched: the streaming kernels split their
+    # contractions further than at 16 tokens
+    counts = _run(moe, "fine_decode", fine_weights, T=T)
+    assert counts.sum() == T * 8
 
 
 def test_fine_prefill_t4096(moe, fine_weights):
