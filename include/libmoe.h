@@ -46,6 +46,11 @@
  *  - Ties in TopK go to the lower expert index; slot 0 of each token holds the
  *    larger logit.  Gates are fp32.
  *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - Diagnostics: with the environment variable LIBMOE_LOG set (to anything
+ *    but "" or "0") when the first call is made, every call that enqueues
+ *    work prints one line to stderr: the entry point, T, D, H, n, K, the
+ *    output type, the expert-product path the shape selects, and the
+ *    returned status.  Unset, it costs one atomic load per call.
  */
 #ifndef LIBMOE_H
 #define LIBMOE_H

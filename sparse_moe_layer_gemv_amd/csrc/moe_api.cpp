@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <atomic>
 #include <functional>
 #include <mutex>
@@ -194,6 +196,40 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   return MOE_OK;
 }
 
+
+// LIBMOE_LOG set to anything but "" or "0": every call that enqueues work
+// prints one line to stderr (entry point, shape, the expert-product path the
+// shape selects, returned status).  Read once; off costs one atomic load.
+bool log_enabled() {
+  static std::atomic<int> state{-1};
+  int v = state.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("LIBMOE_LOG");
+    v = (e && e[0] && !(e[0] == '0' && e[1] == 0)) ? 1 : 0;
+    state.store(v, std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+moe_status_t logged(const char* fn, const moe_problem_t* p, moe_status_t st) {
+  if (!log_enabled()) return st;
+  if (!p) {
+    std::fprintf(stderr, "libmoe: %s problem=null -> %d\n", fn, int(st));
+    return st;
+  }
+  Shape s;
+  const bool ok = check_problem(p, &s) == MOE_OK;
+  std::fprintf(stderr, "libmoe: %s T=%d D=%d H=%d n=%d K=%d out=%s path=%s -> %d (%s)\n", fn,
+               p->tokens, p->dim, p->hidden, p->n_experts, p->top_k,
+               p->out_dtype == MOE_BF16 ? "bf16" : "f32",
+               !ok ? "-" : (s.stream ? "stream" : "tiled"), int(st),
+               st == MOE_OK ? "ok" : st == MOE_EINVAL ? "invalid argument"
+               : st == MOE_ENOTSUP ? "unsupported shape"
+               : st == MOE_EWORKSPACE ? "workspace missing or too small"
+               : st == MOE_EHIP ? "HIP launch failed" : "unknown status");
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,7 +265,7 @@ size_t moe_route_workspace_bytes(const moe_problem_t* p) {
   return moe::route_scratch_bytes(s);
 }
 
-moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate,
+static moe_status_t moe_route_impl(const moe_problem_t* p, const void* x, const void* w_gate,
                        int32_t* topk_idx, float* topk_gate, float* logits, void* ws,
                        size_t ws_bytes, void* stream) {
   Shape s;
@@ -248,7 +284,7 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate
                                       static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* expert_count,
+static moe_status_t moe_permute_impl(const moe_problem_t* p, const int32_t* topk_idx, int32_t* expert_count,
                          int32_t* expert_offset, int32_t* row_slot, int32_t* slot_row,
                          void* stream) {
   Shape s;
@@ -263,7 +299,7 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
                                         slot_row, static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_t* expert_count,
+static moe_status_t moe_grouped_ffn_impl(const moe_problem_t* p, const void* x, const int32_t* expert_count,
                              const int32_t* expert_offset, const int32_t* row_slot,
                              const void* w1, const void* w3, const void* w2, float* y_rows,
                              void* ws, size_t ws_bytes, void* stream) {
@@ -293,7 +329,7 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_
                                          nsplit - 1, size_t(s.cap) * s.D, hs));
 }
 
-moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int32_t* slot_row,
+static moe_status_t moe_combine_impl(const moe_problem_t* p, const float* y_rows, const int32_t* slot_row,
                          const float* topk_gate, void* out, void* stream) {
   Shape s;
   moe_status_t st = check_problem(p, &s);
@@ -307,7 +343,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int3
                                         static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_route_stats(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+static moe_status_t moe_route_stats_impl(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
                              void* stream) {
   Shape s;
   moe_status_t st = check_problem(p, &s);
@@ -317,15 +353,22 @@ moe_status_t moe_route_stats(const moe_problem_t* p, const int32_t* topk_idx, in
   return hip_status(moe::launch_route_stats(s, topk_idx, counts, static_cast<hipStream_t>(stream)));
 }
 
+static moe_status_t moe_forward_timed_impl(const moe_problem_t* p, const void* x,
+                                           const void* w_gate, const void* w1, const void* w3,
+                                           const void* w2, void* out, int32_t* topk_idx,
+                                           float* topk_gate, void* ws, size_t ws_bytes,
+                                           void* stream, void* const* events);
+
 moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* w_gate,
                          const void* w1, const void* w3, const void* w2, void* out,
                          int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
                          void* stream) {
-  return moe_forward_timed(p, x, w_gate, w1, w3, w2, out, topk_idx, topk_gate, ws, ws_bytes,
-                           stream, nullptr);
+  return logged("moe_forward", p,
+                moe_forward_timed_impl(p, x, w_gate, w1, w3, w2, out, topk_idx, topk_gate, ws,
+                                       ws_bytes, stream, nullptr));
 }
 
-moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void* w_gate,
+static moe_status_t moe_forward_timed_impl(const moe_problem_t* p, const void* x, const void* w_gate,
                                const void* w1, const void* w3, const void* w2, void* out,
                                int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
                                void* stream, void* const* events) {
@@ -379,7 +422,7 @@ moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void
   return MOE_OK;
 }
 
-moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* x, const void* w_gate,
+static moe_status_t moe_forward_noalloc_impl(const moe_problem_t* p, const void* x, const void* w_gate,
                                  const void* w1, const void* w3, const void* w2, void* out,
                                  int32_t* topk_idx, float* topk_gate, void* stream) {
   Shape s;
@@ -417,6 +460,56 @@ moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* x, const vo
   // nsplit == c.planes: the second product's partials fill the y planes
   return hip_status(moe::launch_combine(s, y, nsplit, part_stride, nullptr, idx, gate, out,
                                         p->out_dtype == MOE_BF16, hs));
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate,
+                       int32_t* topk_idx, float* topk_gate, float* logits, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return logged("moe_route", p, moe_route_impl(p, x, w_gate, topk_idx, topk_gate, logits, ws,
+                                               ws_bytes, stream));
+}
+
+moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* expert_count,
+                         int32_t* expert_offset, int32_t* row_slot, int32_t* slot_row,
+                         void* stream) {
+  return logged("moe_permute", p, moe_permute_impl(p, topk_idx, expert_count, expert_offset,
+                                                   row_slot, slot_row, stream));
+}
+
+moe_status_t moe_grouped_ffn(const moe_problem_t* p, const void* x, const int32_t* expert_count,
+                             const int32_t* expert_offset, const int32_t* row_slot,
+                             const void* w1, const void* w3, const void* w2, float* y_rows,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return logged("moe_grouped_ffn", p,
+                moe_grouped_ffn_impl(p, x, expert_count, expert_offset, row_slot, w1, w3, w2,
+                                     y_rows, ws, ws_bytes, stream));
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const float* y_rows, const int32_t* slot_row,
+                         const float* topk_gate, void* out, void* stream) {
+  return logged("moe_combine", p, moe_combine_impl(p, y_rows, slot_row, topk_gate, out, stream));
+}
+
+moe_status_t moe_route_stats(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                             void* stream) {
+  return logged("moe_route_stats", p, moe_route_stats_impl(p, topk_idx, counts, stream));
+}
+
+moe_status_t moe_forward_timed(const moe_problem_t* p, const void* x, const void* w_gate,
+                               const void* w1, const void* w3, const void* w2, void* out,
+                               int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                               void* stream, void* const* events) {
+  return logged("moe_forward_timed", p,
+                moe_forward_timed_impl(p, x, w_gate, w1, w3, w2, out, topk_idx, topk_gate, ws,
+                                       ws_bytes, stream, events));
+}
+
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* x, const void* w_gate,
+                                 const void* w1, const void* w3, const void* w2, void* out,
+                                 int32_t* topk_idx, float* topk_gate, void* stream) {
+  return logged("moe_forward_noalloc", p,
+                moe_forward_noalloc_impl(p, x, w_gate, w1, w3, w2, out, topk_idx, topk_gate,
+                                         stream));
 }
 
 }  // extern "C"

@@ -142,3 +142,31 @@ def test_binding_rejects_cpu_tensors(moe):
         moe.route(x, torch.zeros((128, 8), dtype=torch.bfloat16), 2,
                   topk_idx=torch.zeros((4, 2), dtype=torch.int32),
                   topk_gate=torch.zeros((4, 2)))
+
+
+def test_libmoe_log_prints_one_line_per_call(moe):
+    # LIBMOE_LOG in a child process: a valid zero-token forward (no GPU work)
+    # and an invalid one (K > n) each print one line with the status; without
+    # the variable nothing is printed
+    code = (
+        "import ctypes, sparse_moe_layer_gemv_amd as m\n"
+        "p = m.problem(0, 512, 1024, 8, 2)\n"
+        "q = m.problem(16, 512, 1024, 8, 9)\n"
+        "print(m.lib.moe_forward(ctypes.byref(p), None, None, None, None, None, None, None,"
+        " None, None, 0, None))\n"
+        "print(m.lib.moe_forward(ctypes.byref(q), None, None, None, None, None, None, None,"
+        " None, None, 0, None))\n")
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    on = subprocess.run(["python3", "-c", code], capture_output=True, text=True, cwd=ROOT,
+                        env=dict(env, LIBMOE_LOG="1"), timeout=300)
+    assert on.returncode == 0, on.stderr
+    assert on.stdout.split() == [str(moe.MOE_OK), str(moe.MOE_EINVAL)]
+    lines = [l for l in on.stderr.splitlines() if l.startswith("libmoe: ")]
+    assert lines == [
+        "libmoe: moe_forward T=0 D=512 H=1024 n=8 K=2 out=f32 path=stream -> 0 (ok)",
+        "libmoe: moe_forward T=16 D=512 H=1024 n=8 K=9 out=f32 path=- -> 1 (invalid argument)",
+    ]
+    off = subprocess.run(["python3", "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         env=dict(env, LIBMOE_LOG="0"), timeout=300)
+    assert off.returncode == 0, off.stderr
+    assert not [l for l in off.stderr.splitlines() if l.startswith("libmoe: ")]
