@@ -56,6 +56,34 @@ int main(void) {
   CHECK(moe_forward(NULL, fake, fake, fake, fake, fake, fake, NULL, NULL, fake, ws, NULL) ==
         MOE_EINVAL);
 
+  /* every enqueueing entry point: bad problems, null or misaligned pointers
+   * and missing workspaces are refused before anything is enqueued */
+  void* odd = (void*)(uintptr_t)0x100004;
+  int32_t* fi = (int32_t*)fake;
+  float* ff = (float*)fake;
+  CHECK(moe_route_workspace_bytes(&bad) == 0);
+  CHECK(moe_route(&bad, fake, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EINVAL);
+  CHECK(moe_route(&p, NULL, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EINVAL);
+  CHECK(moe_route(&p, odd, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EINVAL);
+  CHECK(moe_route(&p, fake, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EWORKSPACE);
+  CHECK(moe_permute(&p, NULL, fi, fi, fi, fi, NULL) == MOE_EINVAL);
+  CHECK(moe_permute(&bad, fi, fi, fi, fi, fi, NULL) == MOE_EINVAL);
+  CHECK(moe_grouped_ffn(&p, fake, fi, fi, fi, fake, fake, fake, ff, NULL, 0, NULL) ==
+        MOE_EWORKSPACE);
+  CHECK(moe_grouped_ffn(&p, fake, fi, fi, fi, odd, fake, fake, ff, fake, ws, NULL) ==
+        MOE_EINVAL);
+  CHECK(moe_combine(&p, NULL, fi, ff, fake, NULL) == MOE_EINVAL);
+  CHECK(moe_combine(&bad, ff, fi, ff, fake, NULL) == MOE_EINVAL);
+  CHECK(moe_route_stats(&p, fi, NULL, NULL) == MOE_EINVAL);
+  CHECK(moe_forward_timed(&bad, fake, fake, fake, fake, fake, fake, NULL, NULL, fake, ws, NULL,
+                          NULL) == MOE_EINVAL);
+  /* the allocation-free form serves the streaming batches only */
+  CHECK(moe_forward_noalloc(&p, fake, fake, fake, fake, fake, fake, NULL, NULL, NULL) ==
+        MOE_ENOTSUP);
+  CHECK(moe_forward_noalloc(&p, NULL, fake, fake, fake, fake, fake, NULL, NULL, NULL) ==
+        MOE_EINVAL);
+  CHECK(strcmp(moe_status_string(MOE_EHIP), "unknown status") != 0);
+
   /* zero tokens: MOE_OK and nothing is enqueued */
   moe_problem_t empty = p;
   empty.tokens = 0;
