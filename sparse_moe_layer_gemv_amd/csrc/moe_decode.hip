@@ -283,17 +283,28 @@ void launch_decode_rg(const Shape& s, dim3 grid, const uint16_t* x, const float*
                      ab_parts);
 }
 
-// Column blocks per workgroup and contraction splits, by measurement (decode,
-// T = 16; first product + second product):
-//  - wide experts (H = 14336, 112 column blocks per matrix): two blocks per
-//    workgroup and no split in the first product (896 workgroups, 512 bytes of
-//    each weight row at once), two blocks in the second: 293 + 149 us, against
-//    295 + 154 with one block each, and 294-297 + 157 with the first product
-//    split in two (the second then adds two partials of a and b);
+// Column blocks per workgroup and contraction splits, by measurement (layer
+// time at Mixtral decode weights; first product + second product where given):
+//  - wide experts (H = 14336, 112 column blocks per matrix) once every expert
+//    is likely touched (T*K >= 4n): four blocks per workgroup (448
+//    workgroups, all resident at once, where 896 ran in 1.75 rounds) on the
+//    half-wave kernel, no split.  Against two blocks: 16 tokens 435 against
+//    457 us, 24: 444 against 481, 32: 451 against 484, 48 (forced streaming
+//    before): 477 against 561;
+//  - wide experts with fewer tokens: two blocks per workgroup (512 bytes of
+//    each weight row at once).  At 8 tokens (about 7 of 8 experts touched)
+//    four blocks were slower, 345 against 331 us.  Two blocks against one at
+//    16 tokens: 293 + 149 us against 295 + 154; splitting the first product
+//    in two there (the second then adds two partials of a and b): 294-297 +
+//    157.  When few experts can be touched the contraction is split further
+//    (decode_up_splits, decode_down_splits);
 //  - narrow experts (H = 768, 6 blocks): one block and the first product's
 //    contraction split in two (more workgroups): 175 + 97 us, against 183 + 96
 //    unsplit and 201 + 92 with two blocks unsplit.
-int up_blocks(const Shape& s) { return (s.H + 127) / 128 >= 32 ? 2 : 1; }
+int up_blocks(const Shape& s) {
+  if ((s.H + 127) / 128 < 32) return 1;
+  return int64_t(s.T) * s.K >= 4 * int64_t(s.n) ? 4 : 2;
+}
 
 template <bool UP, int WAVES, int NB>
 hipError_t launch_decode_nb(const Shape& s, const uint16_t* x, const float* ab,
@@ -314,7 +325,10 @@ hipError_t launch_decode_nb(const Shape& s, const uint16_t* x, const float* ab,
   // more token rows per lane means more accumulators: fewer waves, so the
   // registers fit without spilling
   static_assert(kStreamMaxTokens <= 4 * kDecodeRows, "four row groups per lane at most");
-  if (s.T <= kDecodeRows)
+  // four column blocks per workgroup run on the half-wave shape at any T:
+  // each wave then walks the whole contraction of its block, with no
+  // reduction across waves (16 tokens: 435 against 450 us per layer)
+  if (s.T <= kDecodeRows && NB != 4)
     launch_decode_rg<UP, 1, WAVES, NB>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
                                        y_part, Kdim, Ndim, P, ncb, nsplit, klen, split_stride,
                                        ab_parts, stream);
@@ -335,6 +349,12 @@ hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const float* ab, c
                            const uint16_t* w0, const uint16_t* w1, void* out, float* y_part,
                            int Kdim, int Ndim, int nsplit, size_t split_stride, int ab_parts,
                            int nb, hipStream_t stream) {
+  if constexpr (UP && WAVES >= 8) {
+    if (nb == 4)
+      return launch_decode_nb<UP, WAVES, 4>(s, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                            y_part, Kdim, Ndim, nsplit, split_stride, ab_parts,
+                                            stream);
+  }
   if (nb == 2)
     return launch_decode_nb<UP, WAVES, 2>(s, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
                                           y_part, Kdim, Ndim, nsplit, split_stride, ab_parts,
@@ -352,6 +372,7 @@ int touched_max(const Shape& s) { return std::min(s.n, s.T * s.K); }
 // ones split while too few experts are touched to give the chip kWantActive
 // workgroups, as long as each wave keeps at least 4 of the 32-deep steps.
 int decode_up_splits(const Shape& s) {
+  if (up_blocks(s) == 4) return 1;
   if (up_blocks(s) == 1) return s.D % 64 == 0 && s.D / 2 >= 32 * 4 * kUpWaves ? 2 : 1;
   const int per = ((s.H + 127) / 128 + 1) / 2 * 2;  // workgroups per expert and split
   int n = 1;
@@ -363,7 +384,7 @@ int decode_up_splits(const Shape& s) {
 
 // Two column blocks per workgroup in the second product for wide outputs.
 int down_blocks(const Shape& s) {
-  return (up_blocks(s) == 2 || decode_up_splits(s) == 1) && (s.D + 127) / 128 >= 2 ? 2 : 1;
+  return (up_blocks(s) >= 2 || decode_up_splits(s) == 1) && (s.D + 127) / 128 >= 2 ? 2 : 1;
 }
 
 }  // namespace

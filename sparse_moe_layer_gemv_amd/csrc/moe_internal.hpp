@@ -17,10 +17,11 @@ constexpr int kMaxExperts = 256;
 // then holds at most 64 token rows (4 groups of 16 per lane).
 constexpr int kStreamMaxTokens = 64;
 // Largest T for which the automatic path choice streams: the small-batch sweep
-// (Mixtral shape) measures streaming faster up to T = 32 (488 against 492 us)
-// and the tiled path faster from T = 48 on (494 against 566 us), since
-// experts of at most 128 rows run as 128- or 64-row tiles.
-constexpr int kDecodeMaxTokens = 32;
+// (Mixtral shape) measures streaming faster up to T = 48 (477 against 490 us)
+// and the tiled path faster from T = 56 (491 against 494-498 us), with four
+// column blocks per first-product workgroup once every expert is likely
+// touched and experts of at most 128 rows as 128- or 64-row tiles.
+constexpr int kDecodeMaxTokens = 48;
 // Token rows handled together by one decode pass (one 16x16 MFMA column block).
 constexpr int kDecodeRows = 16;
 

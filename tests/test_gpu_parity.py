@@ -55,9 +55,18 @@ SHAPES = [
     ("decode_t16", 16, 512, 1024, 8, 2, 15),
     ("decode_t17", 17, 512, 1024, 8, 2, 16),
     ("decode_t32", 32, 384, 640, 8, 2, 17),
-    ("tiled_t33", 33, 512, 1024, 8, 2, 18),
-    ("tiled_t48", 48, 512, 1024, 8, 2, 26),
+    # the automatic streaming threshold (48 tokens) from both sides
+    ("decode_t33", 33, 512, 1024, 8, 2, 18),
+    ("decode_t48", 48, 512, 1024, 8, 2, 26),
     ("tiled_t49", 49, 512, 1024, 8, 2, 27),
+    # wide experts (at least 32 column blocks): two column blocks per
+    # first-product workgroup below T*K = 4n, four from there (16, 24 and 48
+    # tokens: one, two and four row groups per lane), then the tiled path
+    ("stream_wide_t12", 12, 512, 4096, 8, 2, 46),
+    ("stream_wide_t24", 24, 512, 4096, 8, 2, 47),
+    ("stream_wide_t48", 48, 512, 4096, 8, 2, 48),
+    ("tiled_wide_t49", 49, 512, 4096, 8, 2, 49),
+    ("stream_wide_n16_t16", 16, 512, 4096, 16, 2, 50),
     ("k1_switch", 200, 256, 512, 8, 1, 19),
     ("n16_k4", 130, 256, 384, 16, 4, 20),
     ("n6_k3", 90, 136, 200, 6, 3, 21),
