@@ -167,7 +167,7 @@ def crossover(args, torch, moe):
     stream = torch.cuda.current_stream()
     ev = HipEvents()
     rows = []
-    for T in (1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 192, 256):
+    for T in (1, 2, 4, 8, 16, 24, 32, 48, 64, 80, 96, 112, 128, 192, 256):
         x = to_dev(moe_synth.make_x(w.x_seed, T, D))
         idx = torch.empty((T, K), dtype=torch.int32, device="cuda:0")
         out = torch.empty((T, D), dtype=torch.float32, device="cuda:0")

@@ -68,6 +68,8 @@ extern "C" {
  * hold its token-slots. */
 #define MOE_TILE_M 256
 #define MOE_MAX_EXPERTS 256
+/* Largest T the weight-streaming expert path takes (path STREAM). */
+#define MOE_STREAM_MAX_TOKENS 128
 
 typedef enum {
   MOE_OK = 0,
@@ -86,7 +88,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
 /* Expert-product path.  AUTO takes the weight-streaming kernels for
  * T <= moe_decode_max_tokens() and the tiled matrix-core kernels above.
- * STREAM forces the weight-streaming path (T <= 64, MOE_ENOTSUP above); TILED
+ * STREAM forces the weight-streaming path (T <= MOE_STREAM_MAX_TOKENS,
+ * MOE_ENOTSUP above); TILED
  * forces the tiled path at any T.  Both give results within the same
  * tolerance of the exact layer; they are not bit-identical to each other. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_TILED = 2 } moe_path_t;
@@ -236,12 +239,14 @@ int32_t moe_decode_max_tokens(void);
  * each GPU the library runs on holds until the process ends.  The call
  * allocates and frees nothing.
  *   Accepted: the batches moe_forward streams (T <= moe_decode_max_tokens()
- *   with path AUTO, T <= 64 with path STREAM) whose intermediates fit the
- *   array: about 4*T*K*(2 + 2*S1*H + S2*D) bytes, S1 = 1, 2 or 4
- *   first-product partials and S2 = 1..8 second-product partials (the larger
- *   counts when few experts can be touched, i.e. small T*K).  Mixtral's shape
- *   (D = 4096, H = 14336, K = 2) needs 23 MB at T = 64.  Other shapes, and
- *   path TILED, return MOE_ENOTSUP with nothing enqueued.
+ *   with path AUTO, T <= MOE_STREAM_MAX_TOKENS with path STREAM) whose
+ *   intermediates fit the
+ *   array: about 4*T*K*(2 + (2*S1 + 1/2)*H + S2*D) bytes: the first
+ *   product's fp32 a and b in S1 = 1, 2 or 4 contraction partials, bf16 h,
+ *   and S2 = 1..8 second-product partials (the larger counts when few experts
+ *   can be touched, i.e. small T*K).  Mixtral's shape (D = 4096, H = 14336,
+ *   K = 2) needs 27 MB at T = 64.  Other shapes, and path TILED, return
+ *   MOE_ENOTSUP with nothing enqueued.
  *   stream must belong to the calling thread's current device (MOE_EINVAL
  *   otherwise).
  * Every call on one GPU uses that GPU's single array and leaves its contents

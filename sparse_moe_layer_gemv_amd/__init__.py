@@ -27,6 +27,7 @@ MOE_F32, MOE_BF16 = 0, 1
 PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
 TILE_M = 256
 MAX_EXPERTS = 256
+STREAM_MAX_TOKENS = 128
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 EXPORTED = ("moe_capacity_rows", "moe_workspace_bytes", "moe_status_string", "moe_route",
@@ -268,7 +269,7 @@ def forward(x, w_gate, w1, w3, w2, top_k: int, out=None, topk_idx=None, topk_gat
 
     ``events``: optional sequence of 6 raw hipEvent_t handles (None entries
     are skipped); then moe_forward_timed records them between the stages.  ``path``: PATH_AUTO,
-    PATH_STREAM (weight streaming, T <= 64) or PATH_TILED."""
+    PATH_STREAM (weight streaming, T <= STREAM_MAX_TOKENS) or PATH_TILED."""
     torch = _torch()
     p = _shape_of(x, w1, top_k, out_dtype, path)
     T, D, H, n = p.tokens, p.dim, p.hidden, p.n_experts

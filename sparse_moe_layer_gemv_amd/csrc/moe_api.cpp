@@ -20,6 +20,7 @@ using moe::Shape;
 
 static_assert(moe::kMaxExperts == MOE_MAX_EXPERTS, "one expert limit for every kernel");
 static_assert(moe::kTileM == MOE_TILE_M, "one segment granule");
+static_assert(moe::kStreamMaxTokens == MOE_STREAM_MAX_TOKENS, "one streaming limit");
 
 constexpr size_t kAlign = 256;
 
@@ -65,9 +66,9 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
 //   count     int32 [n]       offset    int32 [n+1]
 //   row_slot  int32 [cap]     slot_row  int32 [T*K]
 //   h         bf16  [cap][H]  y_rows    fp32  [S][cap][D] (split partials: S = 2, or
-//                                           up to 4 on the weight-streaming path)
-// With the weight-streaming path the h region holds the fp32 first-product
-// results instead (decode_scratch_bytes).  The router's partial logits
+//                                           up to 8 on the weight-streaming path)
+// With the weight-streaming path the h region holds that path's first-product
+// results instead (bf16 h or fp32 a and b per token-slot; decode_scratch_bytes).  The router's partial logits
 // (route_scratch_bytes) use the start of the y_rows region, which is written
 // only after the router has finished with them.
 struct Carve {
@@ -176,9 +177,8 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   const uint16_t* w3b = static_cast<const uint16_t*>(w3);
   const uint16_t* w2b = static_cast<const uint16_t*>(w2);
   hipError_t e;
-  float* ab = reinterpret_cast<float*>(h);  // decode: fp32 first products
-  if (use_decode(s)) {
-    e = moe::launch_decode_up(s, xb, count, offset, row_slot, topk_idx, w1b, w3b, ab, st);
+  if (use_decode(s)) {  // first products in the h region (decode_scratch_bytes)
+    e = moe::launch_decode_up(s, xb, count, offset, row_slot, topk_idx, w1b, w3b, h, st);
   } else {
     e = moe::launch_grouped_up(s, xb, count, offset, row_slot, w1b, w3b, h, st);
   }
@@ -186,7 +186,7 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   *nsplit = 1;
   if (use_decode(s)) {
     *nsplit = y_part ? moe::decode_down_splits(s) : 1;
-    e = moe::launch_decode_down(s, count, offset, row_slot, topk_idx, ab, w2b, y_rows, y_part,
+    e = moe::launch_decode_down(s, count, offset, row_slot, topk_idx, h, w2b, y_rows, y_part,
                                 *nsplit, part_stride, st);
   } else {
     *nsplit = y_part ? moe::grouped_down_splits(s) : 1;
@@ -404,7 +404,7 @@ static moe_status_t moe_forward_timed_impl(const moe_problem_t* p, const void* x
                         idx, gate, nullptr, y, hs) != hipSuccess || mark(1) != hipSuccess)
     return MOE_EHIP;
   // The weight-streaming path finds each expert's token-slots in the routing
-  // itself (at most 64 tokens), so it needs no permute pass; its rows of y
+  // itself (at most MOE_STREAM_MAX_TOKENS tokens), so it needs no permute pass; its rows of y
   // are then indexed by slot.
   const bool scan = use_decode(s);
   if ((!scan && moe::launch_permute(s, idx, count, offset, row_slot, slot_row, hs) != hipSuccess) ||

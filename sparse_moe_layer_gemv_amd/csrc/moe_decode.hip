@@ -3,7 +3,7 @@
 // The pages note that a sparse MoE layer pays extra memory loads and loses
 // efficiency at small batch sizes ("Mixtral of Experts", section 3, remark on
 // hardware utilisation; the aipaper.jasonlin.tech summary, limitations).  With
-// T <= 64 tokens each expert sees only a handful of rows, so the expert
+// up to ~100 tokens each expert sees a few dozen rows at most, so the expert
 // products are bound by reading the weights: every touched expert's w1, w3
 // and w2 must cross HBM once and nothing else matters.  These kernels do
 // exactly that read, once, coalesced, with many loads in flight, and use the
@@ -23,11 +23,12 @@
 // and whose B columns are up to 16 token rows of the expert.  The waves'
 // partial sums are reduced through LDS in a fixed tree order (deterministic).
 //
-// First product: w1 and w3 are separate workgroups (twice as many workgroups
-// keep more loads in flight than one workgroup reading both), each writing its
-// fp32 result a = x.w1 or b = x.w3 per token-slot.  Second product: each lane
-// forms its h fragment as bf16(silu(a) * b) while loading it (the same single
-// rounding as the tiled path), and the 14336-deep contraction is split into
+// First product: w1 and w3 are separate workgroups (a workgroup reading both
+// would read half as many contiguous bytes of each matrix row), each writing
+// its fp32 result a = x.w1 or b = x.w3 per token-slot and contraction
+// partial.  A small pass adds the partials and forms h = bf16(silu(a) * b)
+// per token-slot, the same single rounding as the tiled path; the second
+// product reads h as the first reads x, and its contraction is split into
 // partial sums written to separate buffers, added in order by the combine.
 #include <algorithm>
 
@@ -48,11 +49,18 @@ __device__ __forceinline__ uint4 load_weight(const uint16_t* p) {
 constexpr int kUpWaves = 8;
 constexpr int kDownWaves = 16;
 
-// 8 consecutive h values of one token-slot: bf16(silu(a) * b) from the fp32
-// first-product results, which come as `nparts` contraction partials
-// `part_stride` floats apart and are added in order.
-__device__ __forceinline__ uint4 h_fragment(const float* a, const float* b, int nparts,
-                                            size_t part_stride) {
+// h = bf16(silu(a) * b) for every token-slot, from the first product's fp32
+// results ab [nparts][2][P][H] (contraction partials added in order): one
+// thread per 8 consecutive values of a row.  Rows of slots no expert
+// computed hold whatever ab held and are never read.
+__global__ __launch_bounds__(256) void decode_h_kernel(const float* __restrict__ ab,
+                                                       uint16_t* __restrict__ h, size_t n8,
+                                                       int nparts, size_t part_stride,
+                                                       size_t b_offset) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const float* a = ab + i * 8;
+  const float* b = a + b_offset;
   f32x4 a0 = *reinterpret_cast<const f32x4*>(a), a1 = *reinterpret_cast<const f32x4*>(a + 4);
   f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 4);
   for (int u = 1; u < nparts; ++u) {
@@ -63,17 +71,18 @@ __device__ __forceinline__ uint4 h_fragment(const float* a, const float* b, int 
     b0 += *reinterpret_cast<const f32x4*>(bu);
     b1 += *reinterpret_cast<const f32x4*>(bu + 4);
   }
-  return make_uint4(pack_bf16x2(silu(a0[0]) * b0[0], silu(a0[1]) * b0[1]),
-                    pack_bf16x2(silu(a0[2]) * b0[2], silu(a0[3]) * b0[3]),
-                    pack_bf16x2(silu(a1[0]) * b1[0], silu(a1[1]) * b1[1]),
-                    pack_bf16x2(silu(a1[2]) * b1[2], silu(a1[3]) * b1[3]));
+  *reinterpret_cast<uint4*>(h + i * 8) =
+      make_uint4(pack_bf16x2(silu(a0[0]) * b0[0], silu(a0[1]) * b0[1]),
+                 pack_bf16x2(silu(a0[2]) * b0[2], silu(a0[3]) * b0[3]),
+                 pack_bf16x2(silu(a1[0]) * b1[0], silu(a1[1]) * b1[1]),
+                 pack_bf16x2(silu(a1[2]) * b1[2], silu(a1[3]) * b1[3]));
 }
 
-// UP:   x [T][Kdim] bf16 rows gathered through row_slot; w = w1 or w3 (by
-//       workgroup); out = ab fp32 [nsplit][2][P][Ndim] (contraction partial
-//       ks; a at [ks][0], b at [ks][1], row = slot)
-// DOWN: ab rows (ab_parts partials) through row_slot -> h; w = w2; partial ks
-//       of y fp32 [cap][Ndim] at out (ks = 0) or y_part + (ks-1) * split_stride
+// UP:   x [T][Kdim] bf16 rows gathered through row_slot; w = w0 (w1) or w1
+//       (w3) by workgroup; out = ab fp32 [nsplit][2][P][Ndim] (contraction
+//       partial ks; a at [ks][0], b at [ks][1], row = slot)
+// DOWN: x = h bf16 [P][Kdim] (row = slot); w0 = w2; partial ks of y fp32
+//       [cap][Ndim] at out (ks = 0) or y_part + (ks-1) * split_stride
 // Both: partial ks covers contraction rows [ks*klen, +klen).
 //
 // SCAN: the expert's token-slots are found by scanning the routing itself
@@ -83,12 +92,11 @@ __device__ __forceinline__ uint4 h_fragment(const float* a, const float* b, int 
 // from the permuted layout (expert_count, expert_offset, row_slot).
 template <bool UP, int RG, int WAVES, int NB, bool SCAN>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ ab,
-    const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
-    const int32_t* __restrict__ row_slot, const int32_t* __restrict__ topk_idx,
-    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
-    float* __restrict__ y_part, int Kdim, int Ndim, int topk, int P, int ncb, int nsplit,
-    int klen, size_t split_stride, int ab_parts) {
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ expert_count,
+    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ row_slot,
+    const int32_t* __restrict__ topk_idx, const uint16_t* __restrict__ w0,
+    const uint16_t* __restrict__ w1, float* __restrict__ out, float* __restrict__ y_part,
+    int Kdim, int Ndim, int topk, int P, int ncb, int nsplit, int klen, size_t split_stride) {
   constexpr int NACC = RG * 8;                     // f32x4 accumulators per lane
   constexpr int WPG = WAVES / NB;                  // waves per column-block group
   static_assert(WAVES % NB == 0 && (WPG & (WPG - 1)) == 0, "groups of a power of two");
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   const int grp = wave / WPG, wl = wave - grp * WPG;
   const int cb = ((r - mat * per_mat) / nsplit) * NB + grp;
   // SCAN: the expert's slots; every token holds an expert at most once, so
-  // there are at most T <= 64 of them
+  // there are at most T <= kStreamMaxTokens of them
   __shared__ int s_list[kStreamMaxTokens];
   __shared__ int s_cnt;
   int cnt, rbase = 0;
@@ -134,12 +142,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     rbase = expert_offset[e];
   }
   // Pass blockIdx.y covers the expert's token rows [16 RG y, 16 RG (y + 1)).
-  // RG is chosen from T, and an expert holds at most T rows when every token
-  // names it at most once (always so under moe_forward, whose router picks K
-  // distinct experts, and the only case SCAN serves); a caller's layout for
-  // moe_grouped_ffn may name an expert twice for one token, and its rows
-  // beyond the first pass are then taken by the further passes of the grid,
-  // whose workgroups otherwise exit here.
+  // The grid has passes enough for the most rows one expert can hold: T when
+  // every token names it at most once (always so under moe_forward, whose
+  // router picks K distinct experts, and the only case SCAN serves), T*K for
+  // a caller's layout given to moe_grouped_ffn, which may name an expert
+  // twice for one token.  Workgroups of passes past an expert's rows exit
+  // here; a pass that has rows streams the expert's weights again.
   const int jb = blockIdx.y * 16 * RG;
   if (cnt <= jb) return;
   const int n0 = cb * 128;
@@ -148,12 +156,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
   const bool col_ok = cb < ncb && n0 + nbk * 8 < Ndim;
   const int kbeg = ks * klen;
   const int kend = min(Kdim, kbeg + klen);
-  const size_t ab_stride = size_t(2) * P * Kdim;   // DOWN: floats between ab partials
 
   // activation row pointers (token row j = jb + lane % 16 + 16 g of the expert)
   const uint16_t* xrow[RG];
-  const float* arow[RG];
-  const float* brow[RG];
   bool aval[RG];
   int slot_of[RG];
 #pragma unroll
@@ -170,12 +175,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     }
     slot_of[g] = slot;
     const int sl = slot >= 0 ? slot : 0;
-    if (UP) {
-      xrow[g] = x + size_t(sl / topk) * Kdim;
-    } else {
-      arow[g] = ab + size_t(sl) * Kdim;
-      brow[g] = ab + (size_t(P) + sl) * Kdim;
-    }
+    xrow[g] = x + size_t(UP ? sl / topk : sl) * Kdim;
   }
   const uint16_t* wp =
       (UP && mat ? w1 : w0) + size_t(e) * Kdim * Ndim + (cb < ncb ? n0 : 0) + nbk * 8;
@@ -201,12 +201,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (kok && aval[g]) {
-        if (UP)
-          v = *reinterpret_cast<const uint4*>(xrow[g] + kk);
-        else
-          v = h_fragment(arow[g] + kk, brow[g] + kk, ab_parts, ab_stride);
-      }
+      if (kok && aval[g]) v = *reinterpret_cast<const uint4*>(xrow[g] + kk);
       xv[g] = as_bf16x8(v);
     }
     uint4 op[8];
@@ -246,6 +241,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     }
     __syncthreads();
   }
+
   if (wl != 0 || cb >= ncb) return;
 
   // Lane holds token row jb + (lane & 15) + 16 g and, for register q, the 8
@@ -256,7 +252,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
     const int j = jb + (lane & 15) + 16 * g;
     const size_t orow = UP ? size_t(ks * 2 + mat) * P + slot_of[g]
                            : (SCAN ? size_t(slot_of[g]) : size_t(rbase + j));
-    float* plane = UP || ks == 0 ? static_cast<float*>(out) : y_part + (ks - 1) * split_stride;
+    float* plane = UP || ks == 0 ? out : y_part + (ks - 1) * split_stride;
     float* op = plane + orow * Ndim;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -271,16 +267,15 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(
 }
 
 template <bool UP, int RG, int WAVES, int NB>
-void launch_decode_rg(const Shape& s, dim3 grid, const uint16_t* x, const float* ab,
-                      const int32_t* cnt, const int32_t* off, const int32_t* row_slot,
-                      const int32_t* topk_idx, const uint16_t* w0, const uint16_t* w1, void* out,
-                      float* y_part, int Kdim, int Ndim, int P, int ncb, int nsplit, int klen,
-                      size_t split_stride, int ab_parts, hipStream_t stream) {
+void launch_decode_rg(const Shape& s, dim3 grid, const uint16_t* x, const int32_t* cnt,
+                      const int32_t* off, const int32_t* row_slot, const int32_t* topk_idx,
+                      const uint16_t* w0, const uint16_t* w1, float* out, float* y_part, int Kdim,
+                      int Ndim, int P, int ncb, int nsplit, int klen, size_t split_stride,
+                      hipStream_t stream) {
   auto kern = topk_idx ? decode_kernel<UP, RG, WAVES, NB, true>
                        : decode_kernel<UP, RG, WAVES, NB, false>;
-  hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), 0, stream, x, ab, cnt, off, row_slot, topk_idx,
-                     w0, w1, out, y_part, Kdim, Ndim, s.K, P, ncb, nsplit, klen, split_stride,
-                     ab_parts);
+  hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), 0, stream, x, cnt, off, row_slot, topk_idx, w0,
+                     w1, out, y_part, Kdim, Ndim, s.K, P, ncb, nsplit, klen, split_stride);
 }
 
 // Column blocks per workgroup and contraction splits, by measurement (layer
@@ -307,61 +302,63 @@ int up_blocks(const Shape& s) {
 }
 
 template <bool UP, int WAVES, int NB>
-hipError_t launch_decode_nb(const Shape& s, const uint16_t* x, const float* ab,
-                            const int32_t* cnt, const int32_t* off, const int32_t* row_slot,
-                            const int32_t* topk_idx, const uint16_t* w0, const uint16_t* w1,
-                            void* out, float* y_part, int Kdim, int Ndim, int nsplit,
-                            size_t split_stride, int ab_parts, hipStream_t stream) {
+hipError_t launch_decode_nb(const Shape& s, const uint16_t* x, const int32_t* cnt,
+                            const int32_t* off, const int32_t* row_slot, const int32_t* topk_idx,
+                            const uint16_t* w0, const uint16_t* w1, float* out, float* y_part,
+                            int Kdim, int Ndim, int nsplit, size_t split_stride,
+                            hipStream_t stream) {
   const int ncb = (Ndim + 127) / 128;
   const int groups = (ncb + NB - 1) / NB;
   const int P = s.T * s.K;
-  // row passes: one when the experts' slots come from the routing (SCAN: K
-  // distinct experts per token, at most T rows each); enough for P = T*K
-  // rows on one expert when they come from a caller's permuted layout
-  const int rows_per_pass = kDecodeRows * (s.T <= kDecodeRows ? 1 : s.T <= 2 * kDecodeRows ? 2 : 4);
-  const int passes = topk_idx ? 1 : (P + rows_per_pass - 1) / rows_per_pass;
+  // Row groups of 16 token rows per lane (RG): one up to 16 tokens, two up to
+  // 64, four beyond.  Four hold 64 rows in one pass, but their 128
+  // accumulators leave a SIMD room for fewer waves: at 48 and 64 tokens two
+  // row groups with a second pass (whose workgroups find no rows past the
+  // first 32 unless an expert holds more) were faster, 449.7 against 455.0
+  // and 460.1 against 465.1 us per layer.  Beyond 64 tokens an expert's rows
+  // pass 32 too often, and a second pass streams its weights again.  Four column blocks per workgroup run on
+  // the half-wave shape at any T: each wave then walks the whole contraction
+  // of its block, with no reduction across waves (16 tokens: 435 against
+  // 450 us per layer).
+  const int rg = s.T <= kDecodeRows && NB != 4 ? 1 : s.T <= 4 * kDecodeRows ? 2 : 4;
+  // row passes: enough for the most rows one expert can hold, T when the
+  // slots come from the routing (SCAN: K distinct experts per token), P = T*K
+  // when they come from a caller's permuted layout
+  const int rows = topk_idx ? s.T : P;
+  const int passes = (rows + kDecodeRows * rg - 1) / (kDecodeRows * rg);
   const dim3 grid(s.n * groups * (UP ? 2 : 1) * nsplit, passes);
   const int klen = (Kdim + nsplit - 1) / nsplit;
-  // more token rows per lane means more accumulators: fewer waves, so the
-  // registers fit without spilling
-  static_assert(kStreamMaxTokens <= 4 * kDecodeRows, "four row groups per lane at most");
-  // four column blocks per workgroup run on the half-wave shape at any T:
-  // each wave then walks the whole contraction of its block, with no
-  // reduction across waves (16 tokens: 435 against 450 us per layer)
-  if (s.T <= kDecodeRows && NB != 4)
-    launch_decode_rg<UP, 1, WAVES, NB>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
+  if (rg == 1)
+    launch_decode_rg<UP, 1, WAVES, NB>(s, grid, x, cnt, off, row_slot, topk_idx, w0, w1, out,
                                        y_part, Kdim, Ndim, P, ncb, nsplit, klen, split_stride,
-                                       ab_parts, stream);
-  else if (s.T <= 2 * kDecodeRows)
-    launch_decode_rg<UP, 2, WAVES / 2, NB>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1,
-                                           out, y_part, Kdim, Ndim, P, ncb, nsplit, klen,
-                                           split_stride, ab_parts, stream);
+                                       stream);
+  else if (rg == 2)
+    launch_decode_rg<UP, 2, WAVES / 2, NB>(s, grid, x, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                           y_part, Kdim, Ndim, P, ncb, nsplit, klen, split_stride,
+                                           stream);
   else
-    launch_decode_rg<UP, 4, WAVES / 2, NB>(s, grid, x, ab, cnt, off, row_slot, topk_idx, w0, w1,
-                                           out, y_part, Kdim, Ndim, P, ncb, nsplit, klen,
-                                           split_stride, ab_parts, stream);
+    launch_decode_rg<UP, 4, WAVES / 2, NB>(s, grid, x, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                           y_part, Kdim, Ndim, P, ncb, nsplit, klen, split_stride,
+                                           stream);
   return hipGetLastError();
 }
 
 template <bool UP, int WAVES>
-hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const float* ab, const int32_t* cnt,
+hipError_t launch_decode_t(const Shape& s, const uint16_t* x, const int32_t* cnt,
                            const int32_t* off, const int32_t* row_slot, const int32_t* topk_idx,
-                           const uint16_t* w0, const uint16_t* w1, void* out, float* y_part,
-                           int Kdim, int Ndim, int nsplit, size_t split_stride, int ab_parts,
-                           int nb, hipStream_t stream) {
+                           const uint16_t* w0, const uint16_t* w1, float* out, float* y_part,
+                           int Kdim, int Ndim, int nsplit, size_t split_stride, int nb,
+                           hipStream_t stream) {
   if constexpr (UP && WAVES >= 8) {
     if (nb == 4)
-      return launch_decode_nb<UP, WAVES, 4>(s, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
-                                            y_part, Kdim, Ndim, nsplit, split_stride, ab_parts,
-                                            stream);
+      return launch_decode_nb<UP, WAVES, 4>(s, x, cnt, off, row_slot, topk_idx, w0, w1, out,
+                                            y_part, Kdim, Ndim, nsplit, split_stride, stream);
   }
   if (nb == 2)
-    return launch_decode_nb<UP, WAVES, 2>(s, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
-                                          y_part, Kdim, Ndim, nsplit, split_stride, ab_parts,
-                                          stream);
-  return launch_decode_nb<UP, WAVES, 1>(s, x, ab, cnt, off, row_slot, topk_idx, w0, w1, out,
-                                        y_part, Kdim, Ndim, nsplit, split_stride, ab_parts,
-                                        stream);
+    return launch_decode_nb<UP, WAVES, 2>(s, x, cnt, off, row_slot, topk_idx, w0, w1, out, y_part,
+                                          Kdim, Ndim, nsplit, split_stride, stream);
+  return launch_decode_nb<UP, WAVES, 1>(s, x, cnt, off, row_slot, topk_idx, w0, w1, out, y_part,
+                                        Kdim, Ndim, nsplit, split_stride, stream);
 }
 
 // Workgroups that have work when at most min(n, T*K) experts are touched.
@@ -387,10 +384,16 @@ int down_blocks(const Shape& s) {
   return (up_blocks(s) >= 2 || decode_up_splits(s) == 1) && (s.D + 127) / 128 >= 2 ? 2 : 1;
 }
 
+// fp32 a and b ([S][2][P][H]) then bf16 h ([P][H]), each 256-byte aligned
+size_t ab_bytes(const Shape& s) {
+  const size_t P = size_t(s.T) * s.K;
+  return (size_t(decode_up_splits(s)) * 2 * P * s.H * 4 + 255) / 256 * 256;
+}
+
 }  // namespace
 
 size_t decode_scratch_bytes(const Shape& s) {
-  return size_t(decode_up_splits(s)) * 2 * s.T * s.K * s.H * 4;
+  return ab_bytes(s) + size_t(s.T) * s.K * s.H * 2;
 }
 
 int decode_down_splits(const Shape& s) {
@@ -413,34 +416,42 @@ int decode_down_splits(const Shape& s) {
 hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
                             const int32_t* expert_offset, const int32_t* row_slot,
                             const int32_t* topk_idx, const uint16_t* w1, const uint16_t* w3,
-                            float* ab, hipStream_t stream) {
-  return launch_decode_t<true, kUpWaves>(s, x, nullptr, expert_count, expert_offset, row_slot,
-                                         topk_idx, w1, w3, ab, nullptr, s.D, s.H,
-                                         decode_up_splits(s), 0, 1, up_blocks(s), stream);
+                            void* scratch, hipStream_t stream) {
+  return launch_decode_t<true, kUpWaves>(s, x, expert_count, expert_offset, row_slot, topk_idx,
+                                         w1, w3, static_cast<float*>(scratch), nullptr, s.D, s.H,
+                                         decode_up_splits(s), 0, up_blocks(s), stream);
 }
 
 hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
                               const int32_t* expert_offset, const int32_t* row_slot,
-                              const int32_t* topk_idx, const float* ab, const uint16_t* w2,
+                              const int32_t* topk_idx, void* scratch, const uint16_t* w2,
                               float* y_rows, float* y_part, int nsplit, size_t part_stride,
                               hipStream_t stream) {
+  // h from the first product's a and b, then the product with w2
+  const float* ab = static_cast<const float*>(scratch);
+  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(scratch) + ab_bytes(s));
+  const size_t P = size_t(s.T) * s.K;
+  const size_t n8 = P * s.H / 8;
+  hipLaunchKernelGGL(decode_h_kernel, dim3(unsigned((n8 + 255) / 256)), dim3(256), 0, stream, ab, h,
+                     n8, decode_up_splits(s), 2 * P * s.H, P * s.H);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // the most waves (up to kDownWaves) that still give each at least 4 of the
   // 32-deep steps: a short contraction (small experts) over 16 waves would
   // spend its time in the reduction
-  const int ab_parts = decode_up_splits(s);
   const int steps = (s.H + nsplit - 1) / nsplit / 32;
   const int nb = down_blocks(s);
   if (steps >= 4 * kDownWaves / nb)
-    return launch_decode_t<false, kDownWaves>(s, nullptr, ab, expert_count, expert_offset,
-                                              row_slot, topk_idx, w2, nullptr, y_rows, y_part,
-                                              s.H, s.D, nsplit, part_stride, ab_parts, nb, stream);
+    return launch_decode_t<false, kDownWaves>(s, h, expert_count, expert_offset, row_slot,
+                                              topk_idx, w2, nullptr, y_rows, y_part, s.H, s.D,
+                                              nsplit, part_stride, nb, stream);
   if (steps >= 4 * 8 / nb)
-    return launch_decode_t<false, 8>(s, nullptr, ab, expert_count, expert_offset, row_slot,
-                                     topk_idx, w2, nullptr, y_rows, y_part, s.H, s.D, nsplit,
-                                     part_stride, ab_parts, nb, stream);
-  return launch_decode_t<false, 4>(s, nullptr, ab, expert_count, expert_offset, row_slot,
-                                   topk_idx, w2, nullptr, y_rows, y_part, s.H, s.D, nsplit,
-                                   part_stride, ab_parts, nb, stream);
+    return launch_decode_t<false, 8>(s, h, expert_count, expert_offset, row_slot, topk_idx, w2,
+                                     nullptr, y_rows, y_part, s.H, s.D, nsplit, part_stride, nb,
+                                     stream);
+  return launch_decode_t<false, 4>(s, h, expert_count, expert_offset, row_slot, topk_idx, w2,
+                                   nullptr, y_rows, y_part, s.H, s.D, nsplit, part_stride, nb,
+                                   stream);
 }
 
 }  // namespace moe

@@ -13,15 +13,15 @@ namespace moe {
 constexpr int kTileM = 256;
 // Largest number of experts; equals MOE_MAX_EXPERTS.
 constexpr int kMaxExperts = 256;
-// Largest T the weight-streaming (decode) expert path supports: every expert
-// then holds at most 64 token rows (4 groups of 16 per lane).
-constexpr int kStreamMaxTokens = 64;
+// Largest T the weight-streaming (decode) expert path supports (equals
+// MOE_STREAM_MAX_TOKENS): every expert then holds at most 128 token rows,
+// taken in passes of 32 or 64 rows.
+constexpr int kStreamMaxTokens = 128;
 // Largest T for which the automatic path choice streams: the small-batch sweep
-// (Mixtral shape) measures streaming faster up to T = 48 (477 against 490 us)
-// and the tiled path faster from T = 56 (491 against 494-498 us), with four
-// column blocks per first-product workgroup once every expert is likely
-// touched and experts of at most 128 rows as 128- or 64-row tiles.
-constexpr int kDecodeMaxTokens = 48;
+// (Mixtral shape) measures streaming faster up to T = 80 (478-488 against
+// 495-497 us on two boxes), the two paths within 3% of each other at T = 96
+// (489-505 against 499 us), and the tiled path faster from T = 112.
+constexpr int kDecodeMaxTokens = 80;
 // Token rows handled together by one decode pass (one 16x16 MFMA column block).
 constexpr int kDecodeRows = 16;
 
@@ -62,24 +62,28 @@ hipError_t launch_grouped_down(const Shape& s, const int32_t* expert_count,
                                hipStream_t stream);
 
 // Weight-streaming path for small T (every touched expert's weights read once).
-// The first product writes fp32 a = x w1 and b = x w3 per token-slot into
-// `ab` ([S][2][T*K][H], S contraction partials; decode_scratch_bytes); the
-// second adds the partials, forms h = silu(a) * b on the fly and may split its
-// contraction into `nsplit` partial sums (decode_down_splits, at most 4):
-// partial 0 at y_rows, partial ks >= 1 at y_part + (ks-1) * part_stride.
+// The first product writes into `scratch` (decode_scratch_bytes) either
+// h = bf16(silu(x w1) * (x w3)) per token-slot ([T*K][H], wide experts with
+// many tokens) or fp32 a = x w1 and b = x w3 ([S][2][T*K][H], S contraction
+// partials), from which the second product forms h on the fly.  The second
+// product may split its contraction into `nsplit` partial sums
+// (decode_down_splits, at most 8): partial 0 at y_rows, partial ks >= 1 at
+// y_part + (ks-1) * part_stride.
 // Each expert's token-slots come from the permuted layout (expert_count,
 // expert_offset, row_slot; y rows at the permuted row) or, when topk_idx is
 // given, from scanning the routing (the others may be null; y rows at the
 // slot index t*K + k).
 size_t decode_scratch_bytes(const Shape& s);
 int decode_down_splits(const Shape& s);
+// launch_decode_up writes a and b; launch_decode_down forms h in the scratch
+// (one pass over the slots) and runs the second product.
 hipError_t launch_decode_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
                             const int32_t* expert_offset, const int32_t* row_slot,
                             const int32_t* topk_idx, const uint16_t* w1, const uint16_t* w3,
-                            float* ab, hipStream_t stream);
+                            void* scratch, hipStream_t stream);
 hipError_t launch_decode_down(const Shape& s, const int32_t* expert_count,
                               const int32_t* expert_offset, const int32_t* row_slot,
-                              const int32_t* topk_idx, const float* ab, const uint16_t* w2,
+                              const int32_t* topk_idx, void* scratch, const uint16_t* w2,
                               float* y_rows, float* y_part, int nsplit, size_t part_stride,
                               hipStream_t stream);
 

@@ -695,7 +695,7 @@ hipError_t launch_route(const Shape& s, const uint16_t* x, const uint16_t* w_gat
     // (more workgroups, a shorter chain each) takes it from 6.5 to 5.4 us at
     // 16 tokens.  Larger batches keep 4 tokens per workgroup so that each W_g
     // row loaded serves 4 tokens.
-    if (s.n == 8 && s.T <= kStreamMaxTokens)
+    if (s.n == 8 && s.T <= 64)
       return launch_router_t<8, 1, true>(s, x, w_gate, topk_idx, topk_gate, logits, stream);
     if (s.n == 8) return launch_router_t<8, 4, true>(s, x, w_gate, topk_idx, topk_gate, logits, stream);
     if (s.n == 16) return launch_router_t<16, 2, true>(s, x, w_gate, topk_idx, topk_gate, logits, stream);

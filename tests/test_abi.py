@@ -38,6 +38,16 @@ def test_header_declares_the_boundary():
         assert f in names
 
 
+def test_binding_constants_match_the_header(moe):
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define (MOE_[A-Z_]+) \(?([0-9u* ]+)\)?", text))
+    val = lambda k: eval(defs[k].replace("u", ""))
+    assert val("MOE_TILE_M") == moe.TILE_M
+    assert val("MOE_MAX_EXPERTS") == moe.MAX_EXPERTS
+    assert val("MOE_STREAM_MAX_TOKENS") == moe.STREAM_MAX_TOKENS
+    assert val("MOE_NOALLOC_SCRATCH_BYTES") == moe.NOALLOC_SCRATCH_BYTES
+
+
 def test_library_exports_every_declared_symbol(moe):
     out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -68,10 +78,12 @@ def test_capacity_and_workspace(moe):
     assert moe.workspace_bytes(moe.problem(4, 8, (1 << 22) - 8, 8, 2)) > 0
     assert moe.decode_max_tokens() >= 16
     # expert-product path: unknown values are invalid; forced streaming only up
-    # to decode_max_tokens(); its scratch is part of the workspace
+    # to STREAM_MAX_TOKENS; its scratch is part of the workspace
     assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 8, 2, path=3)) == 0
-    assert moe.workspace_bytes(moe.problem(64, 4096, 14336, 8, 2, path=moe.PATH_STREAM)) > 0
-    big = 65
+    assert moe.decode_max_tokens() <= moe.STREAM_MAX_TOKENS
+    assert moe.workspace_bytes(moe.problem(moe.STREAM_MAX_TOKENS, 4096, 14336, 8, 2,
+                                           path=moe.PATH_STREAM)) > 0
+    big = moe.STREAM_MAX_TOKENS + 1
     assert moe.workspace_bytes(moe.problem(big, 4096, 14336, 8, 2, path=moe.PATH_STREAM)) == 0
     assert moe.workspace_bytes(moe.problem(big, 4096, 14336, 8, 2, path=moe.PATH_TILED)) > 0
     assert moe.workspace_bytes(moe.problem(16, 4096, 14336, 8, 2, path=moe.PATH_STREAM)) >= \
@@ -133,6 +145,23 @@ def test_stage_validation_errors(moe):
     z = moe.problem(0, 128, 256, 8, 2)
     assert L.moe_route(ctypes.byref(z), 0, 0, 0, 0, None, None, 0, None) == moe.MOE_OK
     assert L.moe_combine(ctypes.byref(z), 0, 0, 0, 0, None) == moe.MOE_OK
+
+
+def test_noalloc_refuses_before_any_device_call(moe):
+    # Refusals of moe_forward_noalloc come from the host checks alone, before
+    # the device is touched, so they hold here without a GPU: the tiled path,
+    # a batch the automatic choice tiles, and intermediates larger than the
+    # array.  64 tokens of 262144-wide experts need at least T*K*H bf16 values
+    # of h, twice the array.
+    L = moe.lib
+
+    def call(p):
+        return L.moe_forward_noalloc(ctypes.byref(p), *([FAKE] * 6), None, None, None)
+
+    assert call(moe.problem(16, 512, 1024, 8, 2, path=moe.PATH_TILED)) == moe.MOE_ENOTSUP
+    assert call(moe.problem(moe.decode_max_tokens() + 1, 512, 1024, 8, 2)) == moe.MOE_ENOTSUP
+    assert 64 * 2 * 262144 * 2 >= 2 * moe.NOALLOC_SCRATCH_BYTES
+    assert call(moe.problem(64, 1024, 262144, 8, 2, path=moe.PATH_STREAM)) == moe.MOE_ENOTSUP
 
 
 def test_binding_rejects_cpu_tensors(moe):

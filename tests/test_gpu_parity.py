@@ -55,17 +55,23 @@ SHAPES = [
     ("decode_t16", 16, 512, 1024, 8, 2, 15),
     ("decode_t17", 17, 512, 1024, 8, 2, 16),
     ("decode_t32", 32, 384, 640, 8, 2, 17),
-    # the automatic streaming threshold (48 tokens) from both sides
+    # streaming with two row groups per lane (32 rows a pass) up to 64
+    # tokens, four (64 rows) beyond, and the automatic threshold (80 tokens)
+    # from both sides
     ("decode_t33", 33, 512, 1024, 8, 2, 18),
     ("decode_t48", 48, 512, 1024, 8, 2, 26),
-    ("tiled_t49", 49, 512, 1024, 8, 2, 27),
+    ("decode_t65", 65, 512, 1024, 8, 2, 27),
+    ("decode_t80", 80, 512, 1024, 8, 2, 51),
+    ("tiled_t81", 81, 512, 1024, 8, 2, 52),
     # wide experts (at least 32 column blocks): two column blocks per
-    # first-product workgroup below T*K = 4n, four from there (16, 24 and 48
-    # tokens: one, two and four row groups per lane), then the tiled path
+    # first-product workgroup below T*K = 4n, four from there (16, 24, 48 and
+    # 80 tokens: one, two, two and four row groups per lane), then the tiled
+    # path
     ("stream_wide_t12", 12, 512, 4096, 8, 2, 46),
     ("stream_wide_t24", 24, 512, 4096, 8, 2, 47),
     ("stream_wide_t48", 48, 512, 4096, 8, 2, 48),
-    ("tiled_wide_t49", 49, 512, 4096, 8, 2, 49),
+    ("stream_wide_t80", 80, 512, 4096, 8, 2, 49),
+    ("tiled_wide_t81", 81, 512, 4096, 8, 2, 53),
     ("stream_wide_n16_t16", 16, 512, 4096, 16, 2, 50),
     ("k1_switch", 200, 256, 512, 8, 1, 19),
     ("n16_k4", 130, 256, 384, 16, 4, 20),
@@ -289,15 +295,18 @@ def test_grouped_ffn_forced_routing(moe, label, make, T, D, H):
 # slot is then its own row of that expert.  With every token of a 16-token
 # batch on expert 3 twice (32 rows, more than one 16-row pass of the
 # weight-streaming kernels) or thrice on expert 6 at T = 40 (120 rows, two
-# passes of 64), both expert paths must compute every row.
-@pytest.mark.parametrize("T,K,path", [(16, 2, 1), (16, 2, 2), (40, 3, 1), (40, 3, 2)],
-                         ids=["t16_k2_stream", "t16_k2_tiled", "t40_k3_stream", "t40_k3_tiled"])
-def test_grouped_ffn_repeated_expert_per_token(moe, T, K, path):
-    D, H, n = 512, 1024, 8
+# passes of 64), both expert paths must compute every row.  With wide experts
+# (H = 4096) the streaming first product forms h itself.
+@pytest.mark.parametrize("T,K,H,path", [(16, 2, 1024, 1), (16, 2, 1024, 2), (40, 3, 1024, 1),
+                                        (40, 3, 1024, 2), (16, 2, 4096, 1), (40, 3, 4096, 1)],
+                         ids=["t16_k2_stream", "t16_k2_tiled", "t40_k3_stream", "t40_k3_tiled",
+                              "t16_k2_stream_wide", "t40_k3_stream_wide"])
+def test_grouped_ffn_repeated_expert_per_token(moe, T, K, H, path):
+    D, n = 512, 8
     idx = np.zeros((T, K), np.int32)
     idx[:, :] = 3 if K == 2 else 6
     idx[::5, -1] = 1          # a few slots elsewhere
-    L = moe_synth.make_layer(T, D, H, n, K, seed=420 + T)
+    L = moe_synth.make_layer(T, D, H, n, K, seed=420 + T + (0 if H == 1024 else 7))
     d = _upload(L)
     perm = moe.permute(dev_i32(idx), n)
     y_rows = moe.grouped_ffn(d["x"], perm["expert_count"], perm["expert_offset"], perm["row_slot"],
@@ -315,7 +324,7 @@ def test_grouped_ffn_repeated_expert_per_token(moe, T, K, path):
 # moe_grouped_ffn writes the rows that hold token-slots and leaves padding
 # rows as they were, also when the second product's contraction is split and
 # its partials are added afterwards (H = 1024 tiled at T = 900; wide experts
-# streamed at T = 16, 4 partials)
+# streamed at T = 16, 4 partials, the first product forming h itself)
 @pytest.mark.parametrize("T,D,H,path", [(900, 512, 1024, 2), (16, 512, 4096, 1)],
                          ids=["tiled_split", "stream_split4"])
 def test_grouped_ffn_leaves_padding_rows(moe, T, D, H, path):
@@ -382,9 +391,9 @@ def test_zero_tokens_is_a_noop(moe):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("T,path", [(16, 2), (1, 2), (32, 2), (24, 1), (5, 1), (64, 1), (60, 1)],
-                         ids=["tiled_t16", "tiled_t1", "tiled_t32", "stream_t24", "stream_t5",
-                              "stream_t64", "stream_t60"])
+@pytest.mark.parametrize("T,path", [(16, 2), (1, 2), (32, 2), (96, 1), (128, 1), (113, 1)],
+                         ids=["tiled_t16", "tiled_t1", "tiled_t32", "stream_t96", "stream_t128",
+                              "stream_t113"])
 def test_forced_expert_path(moe, T, path):
     # both expert-product paths at batch sizes where the other one is the default
     L = moe_synth.make_layer(T, 512, 1024, 8, 2, seed=90 + T)
@@ -402,13 +411,15 @@ def test_forced_expert_path(moe, T, path):
     assert orep.ok, orep
 
 
-@pytest.mark.parametrize("path", [1, 2], ids=["stream", "tiled"])
-def test_every_token_on_the_same_two_experts(moe, path):
+@pytest.mark.parametrize("path,H", [(1, 1024), (2, 1024), (1, 4096)],
+                         ids=["stream", "tiled", "stream_wide"])
+def test_every_token_on_the_same_two_experts(moe, path, H):
     # 64 copies of one token row: every token routes to the same two experts,
     # so each of them holds all 64 slots (the most the streaming path takes
-    # per expert); every output row must equal the oracle's single-token result
+    # per expert, in two row passes); every output row must equal the
+    # oracle's single-token result
     import dataclasses
-    L = moe_synth.make_layer(64, 512, 1024, 8, 2, seed=95)
+    L = moe_synth.make_layer(64, 512, H, 8, 2, seed=95)
     L = dataclasses.replace(L, x=np.repeat(L.x[:1], 64, axis=0))
     d = _upload(L)
     import torch
@@ -429,12 +440,17 @@ def test_every_token_on_the_same_two_experts(moe, path):
 
 
 def test_stream_path_rejects_large_batches(moe):
-    L = moe_synth.make_layer(65, 128, 256, 8, 2, seed=99)
+    import torch
+    T = moe.STREAM_MAX_TOKENS + 1
+    L = moe_synth.make_layer(T, 128, 256, 8, 2, seed=99)
     d = _upload(L)
-    with pytest.raises(moe.MoeError):
+    # a workspace the tiled path would take: the refusal is the path's limit
+    ws = torch.empty(moe.workspace_bytes(moe.problem(T, 128, 256, 8, 2)), dtype=torch.uint8,
+                     device="cuda:0")
+    with pytest.raises(moe.MoeError) as err:
         moe.forward(d["x"], d["wg"], d["w1"], d["w3"], d["w2"], 2, path=moe.PATH_STREAM,
-                    workspace=__import__("torch").empty(1 << 20, dtype=__import__("torch").uint8,
-                                                        device="cuda:0"))
+                    workspace=ws)
+    assert err.value.status == moe.MOE_ENOTSUP
 
 
 @pytest.mark.parametrize("T,D,H,n,K", [(300, 256, 384, 8, 2), (16, 512, 1024, 8, 2),

@@ -86,11 +86,16 @@ def test_noalloc_refuses_what_does_not_fit(moe):
                                            None, stream)
 
     # the tiled path, a batch the automatic choice tiles, and intermediates
-    # beyond the array (64 tokens of 65536-wide experts need 67 MB of first
-    # products) are refused with nothing launched: the buffer stays zero
+    # beyond the array are refused with nothing launched: the buffer stays
+    # zero.  64 tokens of 262144-wide experts need at least T*K*H bf16 values
+    # of h (the smallest form any first product writes), 64 MiB: checked here
+    # before the call, since an accepted call would run the layer on the
+    # 64 KiB buffer
     assert call(16, 512, 1024, 8, 2, path=moe.PATH_TILED) == moe.MOE_ENOTSUP
     assert call(moe.decode_max_tokens() + 1, 512, 1024, 8, 2) == moe.MOE_ENOTSUP
-    assert call(64, 4096, 65536, 8, 2, path=moe.PATH_STREAM) == moe.MOE_ENOTSUP
+    T, D, H, K = 64, 1024, 262144, 2
+    assert T * K * H * 2 >= 2 * moe.NOALLOC_SCRATCH_BYTES
+    assert call(T, D, H, 8, K, path=moe.PATH_STREAM) == moe.MOE_ENOTSUP
     assert call(0, 512, 1024, 8, 2) == moe.MOE_OK
     torch.cuda.synchronize()
     assert int(buf.count_nonzero()) == 0
