@@ -280,14 +280,15 @@ void launch_decode_rg(const Shape& s, dim3 grid, const uint16_t* x, const int32_
 
 // Column blocks per workgroup and contraction splits, by measurement (layer
 // time at Mixtral decode weights; first product + second product where given):
-//  - wide experts (H = 14336, 112 column blocks per matrix) once every expert
-//    is likely touched (T*K >= 4n): four blocks per workgroup (448
+//  - wide experts (H = 14336, 112 column blocks per matrix) once most experts
+//    are likely touched (T*K >= 2.5 n): four blocks per workgroup (448
 //    workgroups, all resident at once, where 896 ran in 1.75 rounds) on the
-//    half-wave kernel, no split.  Against two blocks: 16 tokens 435 against
-//    457 us, 24: 444 against 481, 32: 451 against 484, 48 (forced streaming
-//    before): 477 against 561;
+//    half-wave kernel, no split.  Against two blocks: 10 tokens 376 against
+//    413 us, 12: 378 against 413, 14: 428 against 446, 16: 435 against 457,
+//    24: 444 against 481, 32: 451 against 484, 48 (forced streaming before):
+//    477 against 561;
 //  - wide experts with fewer tokens: two blocks per workgroup (512 bytes of
-//    each weight row at once).  At 8 tokens (about 7 of 8 experts touched)
+//    each weight row at once).  At 8 tokens (5 to 7 of 8 experts touched)
 //    four blocks were slower, 345 against 331 us.  Two blocks against one at
 //    16 tokens: 293 + 149 us against 295 + 154; splitting the first product
 //    in two there (the second then adds two partials of a and b): 294-297 +
@@ -298,7 +299,7 @@ void launch_decode_rg(const Shape& s, dim3 grid, const uint16_t* x, const int32_
 //    unsplit and 201 + 92 with two blocks unsplit.
 int up_blocks(const Shape& s) {
   if ((s.H + 127) / 128 < 32) return 1;
-  return int64_t(s.T) * s.K >= 4 * int64_t(s.n) ? 4 : 2;
+  return 2 * int64_t(s.T) * s.K >= 5 * int64_t(s.n) ? 4 : 2;
 }
 
 template <bool UP, int WAVES, int NB>
@@ -366,14 +367,20 @@ constexpr int kWantActive = 512;
 int touched_max(const Shape& s) { return std::min(s.n, s.T * s.K); }
 
 // Contraction splits of the first product: narrow experts split in two; wide
-// ones split while too few experts are touched to give the chip kWantActive
+// ones split while too few experts are touched to give the chip enough busy
 // workgroups, as long as each wave keeps at least 4 of the 32-deep steps.
+// The target is kWantActive, doubled for wide experts from T*K >= 2n (with
+// two column blocks): at 8 tokens (5 of 8 experts touched in the benchmark
+// routing) the first product went from 203 to 188 us.  The same doubling for
+// the second product saved 9 us at 8 tokens but cost 9 at 10-14, and for
+// smaller T it cost both products (T = 2: 194 -> 208, T = 4: 236 -> 242).
 int decode_up_splits(const Shape& s) {
   if (up_blocks(s) == 4) return 1;
   if (up_blocks(s) == 1) return s.D % 64 == 0 && s.D / 2 >= 32 * 4 * kUpWaves ? 2 : 1;
   const int per = ((s.H + 127) / 128 + 1) / 2 * 2;  // workgroups per expert and split
+  const int want = int64_t(s.T) * s.K >= 2 * int64_t(s.n) ? 2 * kWantActive : kWantActive;
   int n = 1;
-  while (n < 4 && touched_max(s) * per * n < kWantActive && s.D % (64 * 2 * n) == 0 &&
+  while (n < 4 && touched_max(s) * per * n < want && s.D % (64 * 2 * n) == 0 &&
          s.D / (2 * n) >= 32 * 4 * (kUpWaves / 2))
     n *= 2;
   return n;

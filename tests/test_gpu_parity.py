@@ -64,9 +64,10 @@ SHAPES = [
     ("decode_t80", 80, 512, 1024, 8, 2, 51),
     ("tiled_t81", 81, 512, 1024, 8, 2, 52),
     # wide experts (at least 32 column blocks): two column blocks per
-    # first-product workgroup below T*K = 4n, four from there (16, 24, 48 and
-    # 80 tokens: one, two, two and four row groups per lane), then the tiled
-    # path
+    # first-product workgroup below T*K = 2.5n (9 tokens), four from there
+    # (12, 24, 48 and 80 tokens: two, two, two and four row groups per lane),
+    # then the tiled path
+    ("stream_wide_t9", 9, 512, 4096, 8, 2, 54),
     ("stream_wide_t12", 12, 512, 4096, 8, 2, 46),
     ("stream_wide_t24", 24, 512, 4096, 8, 2, 47),
     ("stream_wide_t48", 48, 512, 4096, 8, 2, 48),
