@@ -70,7 +70,9 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
 // With the weight-streaming path the h region holds that path's first-product
 // results instead (bf16 h or fp32 a and b per token-slot; decode_scratch_bytes).  The router's partial logits
 // (route_scratch_bytes) use the start of the y_rows region, which is written
-// only after the router has finished with them.
+// only after the router has finished with them; so do the tiled first
+// product's split last-round halves (grouped_up_scratch_bytes), consumed
+// before the second product writes there.
 struct Carve {
   size_t idx, gate, count, offset, row_slot, slot_row, h, y, total;
 };
@@ -94,7 +96,8 @@ Carve carve(const Shape& s) {
   if (s.stream) h_bytes = std::max(h_bytes, moe::decode_scratch_bytes(s));
   c.h = o;        o = align_up(o + h_bytes, kAlign);
   c.y = o;
-  o = align_up(o + std::max(size_t(y_planes(s)) * s.cap * s.D * 4, moe::route_scratch_bytes(s)),
+  o = align_up(o + std::max({size_t(y_planes(s)) * s.cap * s.D * 4, moe::route_scratch_bytes(s),
+                             s.stream ? size_t(0) : moe::grouped_up_scratch_bytes(s)}),
                kAlign);
   c.total = o;
   return c;
@@ -167,11 +170,13 @@ using MarkFn = std::function<hipError_t(int)>;
 // permuted layout (count, offset, row_slot) gives them.
 // part_stride: floats between consecutive partials of the streaming path's
 // second product (partial p >= 1 at y_part + (p - 1) * part_stride).
+// up_scratch: workspace the second product has not yet written, for the tiled
+// first product's split last round (may be null).
 moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const int32_t* offset,
                      const int32_t* row_slot, const int32_t* topk_idx, const void* w1,
                      const void* w3, const void* w2, float* y_rows, float* y_part,
-                     size_t part_stride, int* nsplit, uint16_t* h, hipStream_t st,
-                     const MarkFn& mark = nullptr) {
+                     size_t part_stride, int* nsplit, uint16_t* h, void* up_scratch,
+                     size_t up_scratch_bytes, hipStream_t st, const MarkFn& mark = nullptr) {
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* w1b = static_cast<const uint16_t*>(w1);
   const uint16_t* w3b = static_cast<const uint16_t*>(w3);
@@ -180,7 +185,8 @@ moe_status_t run_ffn(const Shape& s, const void* x, const int32_t* count, const 
   if (use_decode(s)) {  // first products in the h region (decode_scratch_bytes)
     e = moe::launch_decode_up(s, xb, count, offset, row_slot, topk_idx, w1b, w3b, h, st);
   } else {
-    e = moe::launch_grouped_up(s, xb, count, offset, row_slot, w1b, w3b, h, st);
+    e = moe::launch_grouped_up(s, xb, count, offset, row_slot, w1b, w3b, h, up_scratch,
+                               up_scratch_bytes, st);
   }
   if (e != hipSuccess || (mark && mark(3) != hipSuccess)) return MOE_EHIP;
   *nsplit = 1;
@@ -323,7 +329,8 @@ static moe_status_t moe_grouped_ffn_impl(const moe_problem_t* p, const void* x, 
   // a split second product leaves its partials beyond the first in the
   // workspace; they are added into y_rows in order
   st = run_ffn(s, x, expert_count, expert_offset, row_slot, nullptr, w1, w3, w2, y_rows, y_part,
-               size_t(s.cap) * s.D, &nsplit, reinterpret_cast<uint16_t*>(base + c.h), hs);
+               size_t(s.cap) * s.D, &nsplit, reinterpret_cast<uint16_t*>(base + c.h), y_part,
+               c.total - c.y, hs);
   if (st != MOE_OK || nsplit == 1) return st;
   return hip_status(moe::launch_add_rows(s, expert_count, expert_offset, y_rows, y_part,
                                          nsplit - 1, size_t(s.cap) * s.D, hs));
@@ -413,7 +420,8 @@ static moe_status_t moe_forward_timed_impl(const moe_problem_t* p, const void* x
   const size_t part_stride = size_t(s.cap) * s.D;
   int nsplit = 1;
   st = run_ffn(s, x, count, offset, row_slot, scan ? idx : nullptr, w1, w3, w2, y,
-               y + part_stride, part_stride, &nsplit, h, hs, events ? MarkFn(mark) : MarkFn());
+               y + part_stride, part_stride, &nsplit, h, y, c.total - c.y, hs,
+               events ? MarkFn(mark) : MarkFn());
   if (st != MOE_OK) return st;
   if (moe::launch_combine(s, y, nsplit, part_stride, scan ? nullptr : slot_row, idx, gate, out,
                           p->out_dtype == MOE_BF16, hs) != hipSuccess ||
@@ -455,7 +463,7 @@ static moe_status_t moe_forward_noalloc_impl(const moe_problem_t* p, const void*
     return MOE_EHIP;
   int nsplit = 1;
   st = run_ffn(s, x, nullptr, nullptr, nullptr, idx, w1, w3, w2, y, y + part_stride, part_stride,
-               &nsplit, reinterpret_cast<uint16_t*>(ab), hs);
+               &nsplit, reinterpret_cast<uint16_t*>(ab), nullptr, 0, hs);
   if (st != MOE_OK) return st;
   // nsplit == c.planes: the second product's partials fill the y planes
   return hip_status(moe::launch_combine(s, y, nsplit, part_stride, nullptr, idx, gate, out,

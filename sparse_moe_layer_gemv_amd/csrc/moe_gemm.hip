@@ -223,6 +223,29 @@ __device__ __forceinline__ bool map_tile(int L, const int32_t* __restrict__ offs
   return true;
 }
 
+// Last-round split of the first product.  With few rows per expert a tile is
+// bound by the weight bytes one compute unit can pull, so when the last round
+// of tiles is at most half full (and at most kSplitMaxRounds full rounds come
+// before it) its tiles run as two halves of the contraction each, on twice as
+// many workgroups: every workgroup of that round streams half a panel.  A
+// half writes its fp32 a and b to `part`, and up_split_fixup_kernel adds the
+// two halves in order and forms h.  Tile t = R G + i of that round (R full
+// rounds of G workgroups) is units R G + 2 i and R G + 2 i + 1.
+constexpr int kSplitMaxRounds = 4;
+constexpr size_t kSplitUnitFloats = size_t(BM) * 2 * SUBN;  // a and b of one tile
+
+struct SplitPlan {
+  int R, tail;
+  bool on;
+};
+__device__ __forceinline__ SplitPlan split_plan(int total, int G, bool enabled) {
+  SplitPlan p;
+  p.R = total / G;
+  p.tail = total - p.R * G;
+  p.on = enabled && p.tail > 0 && 2 * p.tail <= G && p.R <= kSplitMaxRounds;
+  return p;
+}
+
 // Per-lane state of one tile: DMA offsets and LDS read offsets.
 //
 // LDS layouts:
@@ -594,7 +617,7 @@ __device__ __forceinline__ void up_tiles(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ expert_count,
     const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ row_slot,
     const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3, uint16_t* __restrict__ h,
-    int T, int D, int H, int n, int K, int k_shift) {
+    float* __restrict__ part, int T, int D, int H, int n, int K, int k_shift) {
   const int nt_count = (H + SUBN - 1) / SUBN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -615,9 +638,10 @@ __device__ __forceinline__ void up_tiles(
     for (int i = 0; i < A_DMA; ++i) sl[i] = row_slot[row0 + a_dma_row(fmw, wave, i, lane)];
   };
 
-  auto make_ctx = [&](int nt_, int e_, int fmw, const int (&sl)[A_DMA]) {
+  // kp: -1 for a whole tile, else the contraction half it covers
+  auto make_ctx = [&](int nt_, int e_, int fmw, const int (&sl)[A_DMA], int kp) {
     TileCtx c;
-    c.kbase = 0;
+    c.kbase = kp < 0 ? 0 : kp * (ksteps / 2) * BK;
     c.ra = make_rsrc(x, uint32_t(T) * D * 2);
     c.rb = make_rsrc((b_sub_of_wave(wave) ? w3 : w1) + size_t(e_) * wsz, uint32_t(wsz * 2));
 #pragma unroll
@@ -630,7 +654,7 @@ __device__ __forceinline__ void up_tiles(
     c.a_dst = wave * a_rows_per_wave_rt(fmw) * A_ROW;
     setup_b_dma(c, lane, wave, nt_ * SUBN, H);
     setup_reads(c, lane, fmw, wm, sub, cb);
-    set_klast(c, ksteps);
+    set_klast(c, kp < 0 ? ksteps : ksteps / 2);
     return c;
   };
 
@@ -668,6 +692,25 @@ __device__ __forceinline__ void up_tiles(
     for (int i = 0; i < FM; ++i)
       if (i < fmw) store_rows(acc, i, row0 + wm * 32 * fmw + i * 32 + l32, n0);
   };
+  // A contraction half: fp32 a (columns 0..127) and b (128..255) of the
+  // tile's rows, row-major, into unit u's slot of `part`.
+  auto store_part = [&](const f32x16 (&acc)[FM][FN], int u, int fmw) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    float* base = part + size_t(u) * kSplitUnitFloats;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i >= fmw) continue;
+      float* prow = base + size_t(wm * 32 * fmw + i * 32 + l32) * 2 * SUBN;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * 32 + q * 8 + hi * 4;
+        *reinterpret_cast<f32x4*>(prow + col) =
+            f32x4{acc[i][0][q * 4], acc[i][0][q * 4 + 1], acc[i][0][q * 4 + 2], acc[i][0][q * 4 + 3]};
+        *reinterpret_cast<f32x4*>(prow + SUBN + col) =
+            f32x4{acc[i][1][q * 4], acc[i][1][q * 4 + 1], acc[i][1][q * 4 + 2], acc[i][1][q * 4 + 3]};
+      }
+    }
+  };
 
   // Persistent: one workgroup per compute unit walks tiles L, L + G, ... (G a
   // multiple of 8, so L stays on its XCD and the XCD's tile order is
@@ -678,18 +721,35 @@ __device__ __forceinline__ void up_tiles(
   // row slots of the tile after next (A_DMA loads, always, so the first wait
   // of the main loop can count them), the main loop, then the next tile's
   // prologue and this tile's stores.
+  // Work units: tiles, and with the last-round split (EVEN shapes, `part`
+  // given) that round's tiles as two contraction halves each.
+  const int total = (expert_offset[n] / BM) * nt_count;
+  const SplitPlan sp = split_plan(total, gridDim.x, EVEN && part != nullptr);
+  const int split0 = sp.R * int(gridDim.x);  // first unit of the split round
+  const int units = sp.on ? split0 + 2 * sp.tail : total;
+  auto map_unit = [&](int L_, int& mt_, int& nt_, int& e_, int& kp_) -> bool {
+    if (L_ >= units) return false;
+    kp_ = -1;
+    int lt = L_;
+    if (sp.on && L_ >= split0) {
+      kp_ = (L_ - split0) & 1;
+      lt = split0 + ((L_ - split0) >> 1);
+    }
+    return map_tile(lt, expert_offset, n, nt_count, mt_, nt_, e_);
+  };
+
   int L = blockIdx.x;
-  int mt, nt, e;
-  if (!map_tile(L, expert_offset, n, nt_count, mt, nt, e)) return;
+  int mt, nt, e, kp;
+  if (!map_unit(L, mt, nt, e, kp)) return;
   int fmw = tile_fmw<EVEN>(expert_count[e]);
   int row0 = expert_offset[e] + mt * BM;
   int slot[A_DMA];
   load_slots(slot, row0, fmw);
-  TileCtx c = make_ctx(nt, e, fmw, slot);
+  TileCtx c = make_ctx(nt, e, fmw, slot, kp);
   if constexpr (EVEN) prologue_class<true, WNT, G>(c, fmw);
   for (;;) {
-    int mt2 = 0, nt2 = 0, e2 = 0;
-    const bool more = map_tile(L + gridDim.x, expert_offset, n, nt_count, mt2, nt2, e2);
+    int mt2 = 0, nt2 = 0, e2 = 0, kp2 = -1;
+    const bool more = map_unit(L + gridDim.x, mt2, nt2, e2, kp2);
     // a valid tile when there is no next one
     const int fmw2 = more ? tile_fmw<EVEN>(expert_count[e2]) : fmw;
     const int row0_next = more ? expert_offset[e2] + mt2 * BM : row0;
@@ -699,24 +759,67 @@ __device__ __forceinline__ void up_tiles(
 
     f32x16 acc[FM][FN];
     if constexpr (EVEN) {
-      run_class<true, WNT, G, A_DMA>(c, fmw, ksteps, acc);
+      run_class<true, WNT, G, A_DMA>(c, fmw, kp < 0 ? ksteps : ksteps / 2, acc);
     } else {
       run_tile<EVEN, WNT, FM>(c, ksteps, G, acc);
     }
     stage_barrier();  // every wave is past this tile's LDS use
     const int n0 = nt * SUBN;
     if (more) {
-      c = make_ctx(nt2, e2, fmw2, slot);
+      c = make_ctx(nt2, e2, fmw2, slot, kp2);
       asm volatile("" ::: "memory");
       if constexpr (EVEN) prologue_class<true, WNT, G>(c, fmw2);
       asm volatile("" ::: "memory");
     }
-    store_h(acc, row0, n0, fmw);
+    if (kp < 0)
+      store_h(acc, row0, n0, fmw);
+    else
+      store_part(acc, L - split0, fmw);
     if (!more) return;
     L += gridDim.x;
     row0 = row0_next;
     nt = nt2;
     fmw = fmw2;
+    kp = kp2;
+  }
+}
+
+// h for the tiles of a split last round: a = a0 + a1 and b = b0 + b1 from the
+// two halves (in that order), h = bf16(silu(a) * b), for the tile's 64 FMW
+// rows.  Workgroup i takes tile R G + i of that round; the plan is recomputed
+// from the same offsets and grid size the first product used, and nothing
+// runs when it did not split.
+__global__ __launch_bounds__(256) void up_split_fixup_kernel(
+    const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
+    const float* __restrict__ part, uint16_t* __restrict__ h, int H, int n, int G) {
+  const int nt_count = H / SUBN;
+  const SplitPlan sp = split_plan((expert_offset[n] / BM) * nt_count, G, true);
+  const int i = blockIdx.x;
+  if (!sp.on || i >= sp.tail) return;
+  int mt, nt, e;
+  if (!map_tile(sp.R * G + i, expert_offset, n, nt_count, mt, nt, e)) return;
+  const int rows = 64 * tile_fmw<true>(expert_count[e]);
+  const size_t row0 = size_t(expert_offset[e]) + size_t(mt) * BM;
+  const int n0 = nt * SUBN;
+  const float* p0 = part + size_t(2 * i) * kSplitUnitFloats;
+  const float* p1 = p0 + kSplitUnitFloats;
+  for (int q = threadIdx.x; q < rows * (SUBN / 8); q += 256) {
+    const int r = q / (SUBN / 8), c8 = (q % (SUBN / 8)) * 8;
+    const float* a0 = p0 + size_t(r) * 2 * SUBN + c8;
+    const float* a1 = p1 + size_t(r) * 2 * SUBN + c8;
+    float v[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(a0 + 4 * half);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(a1 + 4 * half);
+      const f32x4 y0 = *reinterpret_cast<const f32x4*>(a0 + SUBN + 4 * half);
+      const f32x4 y1 = *reinterpret_cast<const f32x4*>(a1 + SUBN + 4 * half);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * half + j] = silu(x0[j] + x1[j]) * (y0[j] + y1[j]);
+    }
+    *reinterpret_cast<uint4*>(h + (row0 + r) * H + n0 + c8) =
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7]));
   }
 }
 
@@ -725,15 +828,15 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_up_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ expert_count,
     const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ row_slot,
     const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3, uint16_t* __restrict__ h,
-    int T, int D, int H, int n, int K, int k_shift) {
+    float* __restrict__ part, int T, int D, int H, int n, int K, int k_shift) {
   // the wave's group is fixed for the whole launch: waves 0-3 own the first
   // half of every tile's rows, waves 4-7 the rest
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
-    up_tiles<EVEN, WNT, KPOW2, 0>(x, expert_count, expert_offset, row_slot, w1, w3, h, T, D, H, n,
-                                  K, k_shift);
+    up_tiles<EVEN, WNT, KPOW2, 0>(x, expert_count, expert_offset, row_slot, w1, w3, h, part, T,
+                                  D, H, n, K, k_shift);
   else
-    up_tiles<EVEN, WNT, KPOW2, 1>(x, expert_count, expert_offset, row_slot, w1, w3, h, T, D, H, n,
-                                  K, k_shift);
+    up_tiles<EVEN, WNT, KPOW2, 1>(x, expert_count, expert_offset, row_slot, w1, w3, h, part, T,
+                                  D, H, n, K, k_shift);
 }
 
 // ---------------------------------------------------------------------------
@@ -893,15 +996,36 @@ bool weights_streamed(const Shape& s) {
 
 }  // namespace
 
+// The last-round split (see SplitPlan) is for shapes of at most 128 slots per
+// expert on average, where a tile is bound by its weight bytes, and whose
+// contraction halves keep the ping-pong's even step count of at least 4.
+namespace {
+constexpr int kSplitMaxUnits = 256;  // scratch slots: one per workgroup of the round
+bool split_eligible(const Shape& s) {
+  const int ksteps = s.D / BK;
+  return s.H % SUBN == 0 && s.D % (2 * BK) == 0 && ksteps % 4 == 0 && ksteps >= 8 &&
+         int64_t(s.T) * s.K <= int64_t(128) * s.n;
+}
+}  // namespace
+
+size_t grouped_up_scratch_bytes(const Shape& s) {
+  return split_eligible(s) ? size_t(kSplitMaxUnits) * kSplitUnitFloats * sizeof(float) : 0;
+}
+
 hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
                              const int32_t* expert_offset, const int32_t* row_slot,
-                             const uint16_t* w1, const uint16_t* w3, uint16_t* h,
-                             hipStream_t stream) {
+                             const uint16_t* w1, const uint16_t* w3, uint16_t* h, void* scratch,
+                             size_t scratch_bytes, hipStream_t stream) {
   const int mt_max = int(s.cap / BM);
   const int nt = (s.H + SUBN - 1) / SUBN;
   if (mt_max * nt == 0) return hipSuccess;
   const int grid = std::min(mt_max * nt, persistent_workgroups());
   const bool even = (s.H % SUBN == 0) && (s.D % (2 * BK) == 0) && s.D >= 4 * BK;
+  // the last-round split when the scratch holds a slot per workgroup
+  const size_t part_need = size_t(grid) * kSplitUnitFloats * sizeof(float);
+  float* part = split_eligible(s) && scratch && scratch_bytes >= part_need
+                    ? static_cast<float*>(scratch)
+                    : nullptr;
   // slot -> token is a shift when K is a power of two
   const bool pow2 = (s.K & (s.K - 1)) == 0;
   const int k_shift = pow2 ? __builtin_ctz(unsigned(s.K)) : 0;
@@ -915,7 +1039,14 @@ hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* e
                           : (pow2 ? grouped_up_kernel<false, false, true>
                                   : grouped_up_kernel<false, false, false>));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), 0, stream, x, expert_count, expert_offset,
-                     row_slot, w1, w3, h, s.T, s.D, s.H, s.n, s.K, k_shift);
+                     row_slot, w1, w3, h, part, s.T, s.D, s.H, s.n, s.K, k_shift);
+  if (part) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // at most half a round of tiles is split
+    hipLaunchKernelGGL(up_split_fixup_kernel, dim3(grid / 2 > 0 ? grid / 2 : 1), dim3(256), 0,
+                       stream, expert_count, expert_offset, part, h, s.H, s.n, grid);
+  }
   return hipGetLastError();
 }
 

@@ -46,11 +46,15 @@ hipError_t launch_permute(const Shape& s, const int32_t* topk_idx, int32_t* expe
 // Tiled matrix-core path: h = silu(x w1) * (x w3) per expert segment, then
 // y_rows = h w2.  h is bf16 [cap][H] in the workspace.  Experts with at most
 // 128 slots run as one tile of 128 or 64 rows (chosen from expert_count on
-// the device), larger ones as full 256-row tiles.
+// the device), larger ones as full 256-row tiles.  `scratch` (may be null)
+// holds the fp32 halves of a split last round of first-product tiles; it is
+// only read and written between the two launches of this call.
 hipError_t launch_grouped_up(const Shape& s, const uint16_t* x, const int32_t* expert_count,
                              const int32_t* expert_offset, const int32_t* row_slot,
-                             const uint16_t* w1, const uint16_t* w3, uint16_t* h,
-                             hipStream_t stream);
+                             const uint16_t* w1, const uint16_t* w3, uint16_t* h, void* scratch,
+                             size_t scratch_bytes, hipStream_t stream);
+// Scratch that lets launch_grouped_up split its last round (0: never splits).
+size_t grouped_up_scratch_bytes(const Shape& s);
 // The second product may be split along its contraction into nsplit = 2
 // partial sums (see grouped_down_splits): partial 0 at y_rows, partial 1 at
 // y_part (unused, may be null, when nsplit = 1).

@@ -74,6 +74,10 @@ SHAPES = [
     ("stream_wide_t80", 80, 512, 4096, 8, 2, 49),
     ("tiled_wide_t81", 81, 512, 4096, 8, 2, 53),
     ("stream_wide_n16_t16", 16, 512, 4096, 16, 2, 50),
+    # the tiled first product with its last round split along the contraction:
+    # 8 experts x 112 column tiles = 896 tiles, 3 full rounds of 256 and a
+    # half-full fourth whose 128 tiles run as 256 contraction halves
+    ("tiled_split_t100", 100, 512, 14336, 8, 2, 55),
     ("k1_switch", 200, 256, 512, 8, 1, 19),
     ("n16_k4", 130, 256, 384, 16, 4, 20),
     ("n6_k3", 90, 136, 200, 6, 3, 21),
@@ -249,6 +253,28 @@ FORCED = [
     # contraction split in two (H = 1024)
     ("row_classes", None, 1, 512, 1024),
 ]
+
+
+# The tiled first product's last-round split with one full round before it:
+# 300 tokens on 12 of 16 experts (slots of token t on experts 2t and 2t + 1
+# mod 12), 12 row tiles x 32 column tiles = 384 tiles = 256 + 128; the split
+# halves' fp32 partials and the pass that adds them must give every slot's
+# expert output.  (Forced tiling of one token at H = 1024 splits every tile:
+# no full round, test_forced_expert_path.)
+def test_grouped_ffn_split_last_round(moe):
+    T, D, H, n, K = 300, 512, 4096, 16, 2
+    t = np.arange(T)
+    idx = np.stack([(2 * t) % 12, (2 * t + 1) % 12], 1).astype(np.int32)
+    L = moe_synth.make_layer(T, D, H, n, K, seed=57)
+    d = _upload(L)
+    perm = moe.permute(dev_i32(idx), n)
+    y_rows = moe.grouped_ffn(d["x"], perm["expert_count"], perm["expert_offset"], perm["row_slot"],
+                             d["w1"], d["w3"], d["w2"], K, path=moe.PATH_TILED)
+    ref = moe_ref.moe_layer(L.x, L.w_gate, L.w1, L.w3, L.w2, K, forced_idx=idx, return_slots=True)
+    sr = host(perm["slot_row"])
+    orep = parity.check_output(ref["E"], host(y_rows)[sr].reshape(T, K, D))
+    print(f"[split last round] slots max/RMS={orep.max_rel:.3e} mean/RMS={orep.mean_rel:.3e}")
+    assert orep.ok, orep
 
 
 def _forced_counts_case():
