@@ -407,14 +407,21 @@ int decode_down_splits(const Shape& s) {
   // Split the contraction while each part still gives every wave of a group at
   // least 4 of the 32-deep steps; with two column blocks per workgroup, twice
   // as many parts keep the workgroup count.  When few experts are touched,
-  // split further (up to 8) until kWantActive workgroups have work.
+  // split further (up to 8) until kWantActive workgroups have work.  From
+  // T*K >= 2n on (most experts touched) two parts and half that target do:
+  // the 512 workgroups of 16 waves then take one round instead of two, and
+  // the combine adds fewer partials (Mixtral decode weights, layer time: 8
+  // tokens 310 -> 299 us, 32: 438 -> 434, 64: 459 -> 450, 12 and 16 the same;
+  // below 2n it cost 4 tokens 16 us, so smaller batches keep the first rule).
   const int nb = down_blocks(s);
   const int wpg = nb == 2 ? kDownWaves / 2 : kDownWaves;
   const int groups = ((s.D + 127) / 128 + nb - 1) / nb;
+  const bool most = int64_t(s.T) * s.K >= 2 * int64_t(s.n);
   int n = 1;
-  const int want = nb == 2 ? 4 : 2;
+  const int want = nb == 2 && !most ? 4 : 2;
   while (n < want && s.H % (64 * n) == 0 && s.H / (2 * n) >= 32 * 4 * wpg) n *= 2;
-  while (n < 8 && touched_max(s) * groups * n < kWantActive && s.H % (64 * 2 * n) == 0 &&
+  const int active = most ? kWantActive / 2 : kWantActive;
+  while (n < 8 && touched_max(s) * groups * n < active && s.H % (64 * 2 * n) == 0 &&
          s.H / (2 * n) >= 32 * 4 * wpg / 2)
     n *= 2;
   return n;
