@@ -126,10 +126,12 @@ const char* moe_status_string(int32_t status);
  *   logits    fp32 [T][n]      out, optional (NULL to skip)
  *   ws, ws_bytes               scratch of moe_route_workspace_bytes(p) bytes
  *                              (NULL/0 when that is 0; else MOE_EWORKSPACE)
- * Logits accumulate in fp32.  With more than 16 experts, or with at least 2048
- * tokens and a multiple of 4 experts, they are computed on the matrix cores in
- * contraction slices whose partial sums pass through ws and are added in
- * slice order. */
+ * Logits accumulate in fp32.  From 2048 tokens with a multiple of 4 experts
+ * (at most 16), they are computed on the matrix cores; when W_g (D rounded up
+ * to a multiple of 32, times n, in bf16) takes at most 64 KiB, in one pass with
+ * no scratch.  With more than 16 experts, or from 2048 tokens with a larger
+ * W_g, they are computed in contraction slices whose partial sums pass through
+ * ws and are added in slice order. */
 size_t moe_route_workspace_bytes(const moe_problem_t* p);
 moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate,
                        int32_t* topk_idx, float* topk_gate, float* logits, void* ws,

@@ -155,9 +155,9 @@ def route_workspace_bytes(p: Problem) -> int:
 def route(x, w_gate, top_k: int, topk_idx=None, topk_gate=None, logits=None, workspace=None,
           stream=None):
     """moe_route: returns (topk_idx int32 [T][K], topk_gate fp32 [T][K]).  The
-    scratch the matrix-core router needs (more than 16 experts, or at least
-    2048 tokens with a multiple of 4 experts) is taken from `workspace`
-    or allocated here."""
+    scratch the slice-wise matrix-core router needs (more than 16 experts,
+    or at least 2048 tokens with a multiple of 4 experts and W_g over 64 KiB)
+    is taken from `workspace` or allocated here."""
     torch = _torch()
     T, D = x.shape
     n = w_gate.shape[1]

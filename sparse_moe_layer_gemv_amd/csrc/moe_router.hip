@@ -190,10 +190,12 @@ RouterSplit router_split(const Shape& s) {
 
 // Up to 16 experts the vector kernel is faster while the batch is small: it
 // is one launch, and its cost is latency.  From about 2048 tokens it re-reads
-// W_g from L2 once per 4 tokens and the matrix-core path takes over (measured
+// W_g from L2 once per 4 tokens and a matrix-core path takes over (measured
 // with the caches flushed, n = 8, D = 4096: 16.8 vs 15.8 us at T = 2048, 26.0
-// vs 21.5 us at T = 4096; at T <= 1024 the vector kernel wins).  The
-// matrix-core path needs n to be a multiple of 4 below 17 experts.
+// vs 21.5 us at T = 4096 for the slice kernel below; at T <= 1024 the vector
+// kernel wins): the one-launch router_fused_kernel when W_g fits its LDS copy
+// (uses_fused_router, checked first), else the slice kernel and its selection
+// pass.  The matrix-core paths need n to be a multiple of 4 below 17 experts.
 bool uses_matrix_router(const Shape& s) {
   return s.n > 16 || (s.n % 4 == 0 && s.T >= kRingMinTokens);
 }
@@ -642,6 +644,154 @@ void launch_partial(const Shape& s, const RouterSplit& r, const uint16_t* x, con
   else launch_partial_t<2>(s, r, x, wg, part, stream);
 }
 
+// Up to 16 experts (a multiple of 4) from kFusedMinTokens tokens, with W_g
+// (rows rounded up to whole 32-row steps) at most kFusedWBytes: the logits on
+// the matrix cores in one launch, with no partial sums in memory.
+// - A workgroup of kFusedWaves waves owns 16 tokens and splits the contraction
+//   between its waves: wave w takes the w-th share of the 32-deep steps.
+// - W_g is copied once into LDS in its own row-major layout (plain buffer
+//   loads, zeros past its end, and LDS stores), so the transposing reads the
+//   ring kernel uses turn each 32-row step into the A operand of
+//   v_mfma_f32_16x16x32_bf16: 16 expert columns, where the columns past n read
+//   the next rows (or zeros past the end) and their products are dropped.
+// - x goes straight from memory into the B operand (lane: token j16,
+//   contraction elements 8 g .. 8 g + 7 of the step), all of a wave's steps in
+//   flight at once.  Tokens past T read row T-1 and elements past D read
+//   element D-8; their products reach only dropped outputs or zero W_g rows.
+// - The waves' [expert][token] sums are added in wave order through LDS (in the
+//   bytes W_g used), then one lane per token selects the top K exactly as
+//   router_kernel does: strict ">", so the lower index wins a tie, and the
+//   softmax over the kept logits.
+// Measured alone (n = 8, D = 4096, rotating 1 GiB of x, graph replays): 9.0 /
+// 10.6 / 16.3 us at T = 2048 / 4096 / 8192, against 10.3 / 12.9 / 21.3 us for
+// the slice kernel and its selection pass.  Every call costs ~7.5 us even for
+// one workgroup (the vector kernel takes 5 us at T = 16 and 8.2 us at 1024),
+// so smaller batches keep the vector kernel.  4 and 16 waves per workgroup
+// measured the same or slower.
+constexpr int kFusedWaves = 8;
+constexpr int kFusedTokens = 16;
+constexpr int kFusedMinTokens = 2048;
+constexpr int kFusedWBytes = 64 * 1024;        // W_g bytes (whole steps) the LDS copy holds
+constexpr int kFusedFill = kFusedWBytes + 64;  // plus the bytes the last step's reads run past
+constexpr int kFusedThreads = kFusedWaves * 64;
+constexpr int kFusedCopy = (kFusedFill / 16 + kFusedThreads - 1) / kFusedThreads;  // 16 B rounds
+constexpr int kFusedCh = 128 / kFusedWaves;    // x steps a wave holds at once (D = 4096: all)
+
+bool uses_fused_router(const Shape& s) {
+  const size_t wbytes = size_t((s.D + 31) / 32) * 32 * s.n * 2;
+  return s.n % 4 == 0 && s.n <= 16 && s.T >= kFusedMinTokens && wbytes <= size_t(kFusedWBytes);
+}
+
+__global__ __launch_bounds__(kFusedThreads) void router_fused_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T, int D, int n, int K,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits) {
+  // W_g; after the steps, the waves' sums and the logits in the same bytes
+  __shared__ __attribute__((aligned(16))) uint8_t wl[kFusedFill];
+  static_assert(kFusedWaves * 64 * sizeof(f32x4) + kFusedTokens * 17 * sizeof(float) <= kFusedFill,
+                "the sums fit where W_g was");
+  f32x4(*red)[64] = reinterpret_cast<f32x4(*)[64]>(wl);
+  float(*lg)[17] = reinterpret_cast<float(*)[17]>(wl + kFusedWaves * 64 * sizeof(f32x4));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, j16 = lane & 15;
+  const int t0 = blockIdx.x * kFusedTokens;
+  const uint32_t row_bytes = uint32_t(n) * 2;
+  const uint32_t wbytes = uint32_t(D) * row_bytes;
+  const int ksteps = (D + 31) / 32;
+  const int spw = (ksteps + kFusedWaves - 1) / kFusedWaves;
+  const int s0 = min(ksteps, wave * spw), s1 = min(ksteps, s0 + spw);
+  const uint16_t* xrow = x + size_t(min(t0 + j16, T - 1)) * D;
+
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wg, wbytes);
+  u32x4 wv[kFusedCopy];
+#pragma unroll
+  for (int i = 0; i < kFusedCopy; ++i)
+    wv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        rw, int((uint32_t(i) * kFusedThreads + threadIdx.x) * 16), 0, 0);
+  // steps past the wave's share hold zeros, so the step loop below runs
+  // without branches and its LDS reads can be issued ahead
+  uint4 xa[kFusedCh];
+  auto load_round = [&](int r0) {
+#pragma unroll
+    for (int j = 0; j < kFusedCh; ++j) {
+      const int kk = min(32 * (r0 + j) + 8 * g, D - 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(xrow + kk);
+      xa[j] = r0 + j < s1 ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load_round(s0);
+#pragma unroll
+  for (int i = 0; i < kFusedCopy; ++i) {
+    const uint32_t o = (uint32_t(i) * kFusedThreads + threadIdx.x) * 16;
+    if (i + 1 < kFusedCopy || o < uint32_t(kFusedFill)) *reinterpret_cast<u32x4*>(wl + o) = wv[i];
+  }
+  __syncthreads();
+
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  // rows 8 g + (j16 >> 2) and + 4, expert columns 4 (j16 & 3) .. + 3 of a step
+  const uint32_t b_off = uint32_t(8 * g + (j16 >> 2)) * row_bytes + uint32_t(8 * (j16 & 3));
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int r0 = s0; r0 < s1; r0 += kFusedCh) {
+    if (r0 != s0) load_round(r0);
+#pragma unroll
+    for (int j = 0; j < kFusedCh; ++j) {
+      // a step past the end reads the last step's (finite) rows against zeros
+      const uint32_t off = uint32_t(min(r0 + j, ksteps - 1)) * 32 * row_bytes + b_off;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds(wl) + off));
+      const v4i16 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds(wl) + off + 4 * row_bytes));
+      const bf16x8 b =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, as_bf16x8(xa[j]), acc, 0, 0, 0);
+    }
+  }
+
+  // acc[r]: expert 4 g + r of token t0 + j16, over this wave's share
+  __syncthreads();  // every wave is past its W_g reads
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 v = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kFusedWaves; ++w) v += red[w][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lg[j16][4 * g + r] = v[r];
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid >= kFusedTokens || t0 + tid >= T) return;
+  const int tok = t0 + tid;
+  if (logits)
+    for (int e = 0; e < n; ++e) logits[size_t(tok) * n + e] = lg[tid][e];
+  uint32_t taken = 0;
+  float top = 0.f, sum = 0.f;
+  for (int s = 0; s < K; ++s) {
+    int bi = -1;
+    float bv = 0.f;
+    for (int e = 0; e < n; ++e)
+      if (!((taken >> e) & 1u) && (bi < 0 || lg[tid][e] > bv)) {
+        bi = e;
+        bv = lg[tid][e];
+      }
+    taken |= 1u << bi;
+    if (s == 0) top = bv;
+    const float ex = __expf(bv - top);
+    sum += ex;
+    topk_idx[size_t(tok) * K + s] = bi;
+    topk_gate[size_t(tok) * K + s] = ex;
+  }
+  const float inv = 1.f / sum;
+  for (int s = 0; s < K; ++s) topk_gate[size_t(tok) * K + s] *= inv;
+}
+
+hipError_t launch_fused(const Shape& s, const uint16_t* x, const uint16_t* wg, int32_t* idx,
+                        float* gate, float* logits, hipStream_t stream) {
+  hipLaunchKernelGGL(router_fused_kernel, dim3((s.T + kFusedTokens - 1) / kFusedTokens),
+                     dim3(kFusedThreads), 0, stream, x, wg, s.T, s.D, s.n, s.K, idx, gate, logits);
+  return hipGetLastError();
+}
+
 template <int NE, int TPW, bool VEC>
 hipError_t launch_router_t(const Shape& s, const uint16_t* x, const uint16_t* wg, int32_t* idx,
                            float* gate, float* logits, hipStream_t stream) {
@@ -681,7 +831,7 @@ void launch_ring(const Shape& s, const RingSplit& r, const uint16_t* x, const ui
 }  // namespace
 
 size_t route_scratch_bytes(const Shape& s) {
-  if (s.T == 0 || !uses_matrix_router(s)) return 0;
+  if (s.T == 0 || uses_fused_router(s) || !uses_matrix_router(s)) return 0;
   const int S = s.n % 4 == 0 ? ring_split(s).S : router_split(s).S;
   return size_t(S) * s.T * s.n * sizeof(float);
 }
@@ -690,6 +840,8 @@ hipError_t launch_route(const Shape& s, const uint16_t* x, const uint16_t* w_gat
                         int32_t* topk_idx, float* topk_gate, float* logits, float* scratch,
                         hipStream_t stream) {
   if (s.T == 0) return hipSuccess;
+  if (uses_fused_router(s))
+    return launch_fused(s, x, w_gate, topk_idx, topk_gate, logits, stream);
   if (!uses_matrix_router(s)) {
     // Up to 64 tokens the router is pure latency: one token per workgroup
     // (more workgroups, a shorter chain each) takes it from 6.5 to 5.4 us at

@@ -65,7 +65,12 @@ int main(void) {
   CHECK(moe_route(&bad, fake, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EINVAL);
   CHECK(moe_route(&p, NULL, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EINVAL);
   CHECK(moe_route(&p, odd, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EINVAL);
-  CHECK(moe_route(&p, fake, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EWORKSPACE);
+  /* the slice-wise router (here: 160 experts) takes its partial sums from ws */
+  moe_problem_t many = p;
+  many.n_experts = 160;
+  many.top_k = 8;
+  CHECK(moe_route_workspace_bytes(&many) > 0);
+  CHECK(moe_route(&many, fake, fake, fi, ff, NULL, NULL, 0, NULL) == MOE_EWORKSPACE);
   CHECK(moe_permute(&p, NULL, fi, fi, fi, fi, NULL) == MOE_EINVAL);
   CHECK(moe_permute(&bad, fi, fi, fi, fi, fi, NULL) == MOE_EINVAL);
   CHECK(moe_grouped_ffn(&p, fake, fi, fi, fi, fake, fake, fake, ff, NULL, 0, NULL) ==

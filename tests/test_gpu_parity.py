@@ -183,6 +183,29 @@ def test_route_stage_logits_large_n(moe, n, D, T):
     assert rr.ok, rr
 
 
+# Up to 16 experts (a multiple of 4) from 2048 tokens: router_fused_kernel
+# while W_g, D rounded up to whole 32-row steps, fits its 64 KiB LDS copy
+# (ragged token tail, D not a multiple of 32, exactly 64 KiB, two rounds of x
+# steps per wave at D = 8192, K = n); beyond that the slice kernel and its
+# selection pass (n = 16 at D = 4096, n = 8 at D = 8192)
+@pytest.mark.parametrize("n,D,T,K", [(4, 4096, 2048, 1), (8, 4096, 4099, 2), (12, 1000, 2050, 3),
+                                     (16, 2048, 2048, 4), (4, 8192, 2048, 2), (8, 512, 2048, 8),
+                                     (16, 4096, 2048, 2), (8, 8192, 2100, 2)])
+def test_route_matrix_core_paths_up_to_16_experts(moe, n, D, T, K):
+    import torch
+    L = moe_synth.make_layer(T, D, 8, n, K, seed=40 + n + D % 97)
+    x, wg = dev_bf16(L.x), dev_bf16(L.w_gate)
+    logits = torch.empty((T, n), dtype=torch.float32, device="cuda:0")
+    idx, gate = moe.route(x, wg, K, logits=logits)
+    ref = moe_ref.router_logits(L.x, L.w_gate)
+    assert np.abs(host(logits) - ref).max() < 2e-5
+    rr = parity.check_routing(ref, K, host(idx), host(gate))
+    assert rr.ok, rr
+    # without the optional logits output the choice and gates are the same
+    idx2, gate2 = moe.route(x, wg, K)
+    assert np.array_equal(host(idx2), host(idx)) and np.array_equal(host(gate2), host(gate))
+
+
 def test_route_ties_go_to_the_lower_index_with_many_experts(moe):
     # W_g with duplicated columns gives exactly equal logits: the lower expert
     # index must win every tie, slot order by decreasing logit
@@ -197,8 +220,8 @@ def test_route_ties_go_to_the_lower_index_with_many_experts(moe):
     assert np.array_equal(host(idx), want)
 
 
-# T < 2048 takes the vector router (router_kernel), T >= 2048 the matrix-core
-# pair (router_ring_kernel + router_select_kernel) for n = 8
+# T < 2048 takes the vector router (router_kernel), T >= 2048 the one-launch
+# matrix-core router (router_fused_kernel) for n = 8
 @pytest.mark.parametrize("T", [64, 1000, 2048, 4096])
 def test_route_ties_go_to_the_lower_index_with_eight_experts(moe, T):
     # Mixtral's router shape (dim 4096, 8 experts, top-2) with W_g columns 5
