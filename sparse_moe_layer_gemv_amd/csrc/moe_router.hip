@@ -499,16 +499,17 @@ __device__ __forceinline__ void row_argmax(float& bv, int& bi) {
   const float ov = __int_as_float(
       __builtin_amdgcn_update_dpp(0, __float_as_int(bv), kRowRor, 0xF, 0xF, false));
   const int oi = __builtin_amdgcn_update_dpp(0, bi, kRowRor, 0xF, 0xF, false);
-  if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
-    bv = ov;
-    bi = oi;
-  }
+  // selects, not a branch: every lane of the row takes part in the next step
+  const bool take = (oi >= 0) & ((bi < 0) | (ov > bv) | ((ov == bv) & (oi < bi)));
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
 }
 
 // 16 lanes per token, 16 tokens per 256-thread workgroup; lane j16 of a token
 // holds the logits of experts 64 m + 4 j16 + c (c = 0..3, m = 0..NM-1), read
-// as 16-byte vectors when n is a multiple of 4.
-template <int NM, bool VEC4>
+// as 16-byte vectors when n is a multiple of 4.  KQ: slots a lane keeps (slot
+// s in lane s % 16): 1 for K <= 16, else 16.
+template <int NM, bool VEC4, int KQ>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int S, int T, int n, int K, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_gate, float* __restrict__ logits) {
@@ -558,10 +559,10 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   // go to the lower index.  Slot s's expert and e^(l - top) stay in lane
   // s % 16.
   uint32_t taken = 0;  // bit 4 m + c
-  int my_idx[16];
-  float my_ex[16];
+  int my_idx[KQ];
+  float my_ex[KQ];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < KQ; ++q) {
     my_idx[q] = 0;
     my_ex[q] = 0.f;
   }
@@ -574,10 +575,9 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int e = 64 * m + 4 * j16 + c;
-        if (e < n && !((taken >> (4 * m + c)) & 1u) && (bi < 0 || v[m][c] > bv)) {
-          bi = e;
-          bv = v[m][c];
-        }
+        const bool better = (e < n) & !((taken >> (4 * m + c)) & 1u) & ((bi < 0) | (v[m][c] > bv));
+        bi = better ? e : bi;
+        bv = better ? v[m][c] : bv;
       }
     // all-reduce over the 16 lanes of a row by rotations of 8, 4, 2, 1 (the
     // order (value, then lower index) is total, so any combining order gives
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const float ex = __expf(bv - top);
     sum += ex;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
+    for (int q = 0; q < KQ; ++q)
       if (s == 16 * q + j16) {
         my_idx[q] = bi;
         my_ex[q] = ex;
@@ -600,7 +600,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   if (!tok_ok) return;
   const float inv = 1.f / sum;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < KQ; ++q) {
     const int s = 16 * q + j16;
     if (s < K) {
       topk_idx[size_t(t) * K + s] = my_idx[q];
@@ -613,12 +613,18 @@ template <int NM>
 void launch_select_t(const Shape& s, int S, const float* part, int32_t* idx, float* gate,
                      float* logits, hipStream_t stream) {
   const dim3 grid((s.T + 15) / 16), block(256);
-  if (s.n % 4 == 0)
-    hipLaunchKernelGGL((router_select_kernel<NM, true>), grid, block, 0, stream, part, S, s.T, s.n,
-                       s.K, idx, gate, logits);
-  else
-    hipLaunchKernelGGL((router_select_kernel<NM, false>), grid, block, 0, stream, part, S, s.T,
+  if (s.n % 4 == 0 && s.K <= 16)
+    hipLaunchKernelGGL((router_select_kernel<NM, true, 1>), grid, block, 0, stream, part, S, s.T,
                        s.n, s.K, idx, gate, logits);
+  else if (s.n % 4 == 0)
+    hipLaunchKernelGGL((router_select_kernel<NM, true, 16>), grid, block, 0, stream, part, S, s.T,
+                       s.n, s.K, idx, gate, logits);
+  else if (s.K <= 16)
+    hipLaunchKernelGGL((router_select_kernel<NM, false, 1>), grid, block, 0, stream, part, S, s.T,
+                       s.n, s.K, idx, gate, logits);
+  else
+    hipLaunchKernelGGL((router_select_kernel<NM, false, 16>), grid, block, 0, stream, part, S,
+                       s.T, s.n, s.K, idx, gate, logits);
 }
 
 void launch_select(const Shape& s, int S, const float* part, int32_t* idx, float* gate,
