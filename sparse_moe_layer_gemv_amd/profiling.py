@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "grouped_down": ["csrc/moe_gemm.hip", "csrc/moe_device.hpp", "csrc/moe_internal.hpp"],
     "decode_up": ["csrc/moe_decode.hip", "csrc/moe_device.hpp", "csrc/moe_internal.hpp"],
     "decode_down": ["csrc/moe_decode.hip", "csrc/moe_device.hpp", "csrc/moe_internal.hpp"],
+    "router_fused": ["csrc/moe_router.hip", "csrc/moe_device.hpp", "csrc/moe_internal.hpp"],
 }
 
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read, 1 GiB written
