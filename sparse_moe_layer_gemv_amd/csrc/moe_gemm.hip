@@ -409,17 +409,28 @@ __device__ __forceinline__ void tail_step(const TileCtx& c, int s0, int r, Frags
   if (r > I) step<EVEN, WNT, FMW, G, I>(c, s0 + I, f0, f1, acc);
 }
 
-// Prologue of the ping-pong: every wave issues its share of weight steps 0..2
-// and activation blocks 0, 1 (steps 0..3); memory phase s then issues step
-// s + 3 onwards.  The LDS must be free (every wave past its last reads).
-template <bool EVEN, bool WNT, int FMW, int G>
+// Phase of the ring schedule: step s of a tile runs as phase (s + SH) % 12,
+// which fixes its weight stage (phase % 4) and activation block
+// ((phase / 2) % 3).  With ksteps % 12 == 8 (the Mixtral contractions: 128
+// steps, and 224 per half of the second product) the shift SH = 4 runs the
+// first 8 steps as phases 4..11 in straight-line code, and the rest as whole
+// 12-step rounds of the loop, so no step sits in the guarded tail (where the
+// compiler waits for every load in flight before each step's reads).
+constexpr int kShiftSteps = 4;
+__device__ __forceinline__ bool phase_shifted(int ksteps) { return ksteps % 12 == 8; }
+
+// Prologue of the ping-pong: every wave issues its share of the weights of
+// steps 0..2 and of the activation blocks of steps 0..3 (phases SH ..
+// SH + 3); memory phase s then issues step s + 3 onwards.  The LDS must be
+// free (every wave past its last reads).
+template <bool EVEN, bool WNT, int FMW, int G, int SH = 0>
 __device__ __forceinline__ void pp_prologue(const TileCtx& c) {
   constexpr int AD = a_dma<FMW, G>();
-  issue_b<EVEN, WNT>(c, b_stage<0>(), 0);
-  issue_a<EVEN, WNT, 0, AD>(c, a_block<0>(), 0);
-  issue_b<EVEN, WNT>(c, b_stage<1>(), BK);
-  issue_b<EVEN, WNT>(c, b_stage<2>(), 2 * BK);
-  issue_a<EVEN, WNT, 0, AD>(c, a_block<1>(), min(2 * BK, c.klast_a));
+  issue_b<EVEN, WNT>(c, b_stage<SH % NB>(), 0);
+  issue_a<EVEN, WNT, 0, AD>(c, a_block<(SH / 2) % NA>(), 0);
+  issue_b<EVEN, WNT>(c, b_stage<(SH + 1) % NB>(), BK);
+  issue_b<EVEN, WNT>(c, b_stage<(SH + 2) % NB>(), 2 * BK);
+  issue_a<EVEN, WNT, 0, AD>(c, a_block<(SH / 2 + 1) % NA>(), min(2 * BK, c.klast_a));
 }
 
 // Main loop over the contraction (ksteps even, >= 4 steps of 32), after
@@ -427,19 +438,31 @@ __device__ __forceinline__ void pp_prologue(const TileCtx& c) {
 // order; LOADS_AFTER more loads were issued after the prologue's.  Stores may
 // also be pending; they only make the count stricter, so the wait below holds
 // whatever their order relative to the loads.
-template <bool EVEN, bool WNT, int FMW, int G, int LOADS_AFTER>
+template <bool EVEN, bool WNT, int FMW, int G, int LOADS_AFTER, int SH = 0>
 __device__ __forceinline__ void run_tile_pp_main(const TileCtx& c, int ksteps,
                                                  f32x16 (&acc)[FM][FN]) {
+  static_assert(SH == 0 || SH == kShiftSteps, "two schedules");
   // weight step 0 and this wave's share of activation block 0 (the
   // prologue's first 2 + AD loads) landed
   wait_vmcnt<2 * B_DMA + a_dma<FMW, G>() + LOADS_AFTER>();
   stage_barrier();
   Frags<FMW> f0, f1;
   if (G == 0) {
-    read_frags<FMW>(c, a_block<0>(), b_stage<0>(), 0, 0, f0);
-    read_frags<FMW>(c, a_block<0>(), b_stage<0>(), 1, 1, f1);
+    read_frags<FMW>(c, a_block<(SH / 2) % NA>(), b_stage<SH % NB>(), 0, 0, f0);
+    read_frags<FMW>(c, a_block<(SH / 2) % NA>(), b_stage<SH % NB>(), 1, 1, f1);
   }
   int s = 0;
+  if constexpr (SH == kShiftSteps) {  // steps 0..7 as phases 4..11 (ksteps % 12 == 8)
+    step<EVEN, WNT, FMW, G, 4>(c, 0, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 5>(c, 1, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 6>(c, 2, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 7>(c, 3, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 8>(c, 4, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 9>(c, 5, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 10>(c, 6, f0, f1, acc);
+    step<EVEN, WNT, FMW, G, 11>(c, 7, f0, f1, acc);
+    s = 8;
+  }
   for (; s + 12 <= ksteps; s += 12) {
     step<EVEN, WNT, FMW, G, 0>(c, s + 0, f0, f1, acc);
     step<EVEN, WNT, FMW, G, 1>(c, s + 1, f0, f1, acc);
@@ -454,20 +477,22 @@ __device__ __forceinline__ void run_tile_pp_main(const TileCtx& c, int ksteps,
     step<EVEN, WNT, FMW, G, 10>(c, s + 10, f0, f1, acc);
     step<EVEN, WNT, FMW, G, 11>(c, s + 11, f0, f1, acc);
   }
-  // 0..11 remaining steps; s is a multiple of 12, so their stage and block
-  // indices are those of steps 0..10
-  const int r = ksteps - s;
-  tail_step<EVEN, WNT, FMW, G, 0>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 1>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 2>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 3>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 4>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 5>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 6>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 7>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 8>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 9>(c, s, r, f0, f1, acc);
-  tail_step<EVEN, WNT, FMW, G, 10>(c, s, r, f0, f1, acc);
+  // 0..11 remaining steps (none with the shifted schedule); s is a multiple
+  // of 12, so their stage and block indices are those of steps 0..10
+  if constexpr (SH == 0) {
+    const int r = ksteps - s;
+    tail_step<EVEN, WNT, FMW, G, 0>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 1>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 2>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 3>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 4>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 5>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 6>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 7>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 8>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 9>(c, s, r, f0, f1, acc);
+    tail_step<EVEN, WNT, FMW, G, 10>(c, s, r, f0, f1, acc);
+  }
   // the surplus loads must land before the workgroup's LDS is released
   wait_vmcnt<0>();
 }
@@ -475,8 +500,13 @@ __device__ __forceinline__ void run_tile_pp_main(const TileCtx& c, int ksteps,
 template <bool EVEN, bool WNT, int FMW, int G>
 __device__ __forceinline__ void run_tile_pp(const TileCtx& c, int ksteps,
                                             f32x16 (&acc)[FM][FN]) {
-  pp_prologue<EVEN, WNT, FMW, G>(c);
-  run_tile_pp_main<EVEN, WNT, FMW, G, 0>(c, ksteps, acc);
+  if (phase_shifted(ksteps)) {
+    pp_prologue<EVEN, WNT, FMW, G, kShiftSteps>(c);
+    run_tile_pp_main<EVEN, WNT, FMW, G, 0, kShiftSteps>(c, ksteps, acc);
+  } else {
+    pp_prologue<EVEN, WNT, FMW, G>(c);
+    run_tile_pp_main<EVEN, WNT, FMW, G, 0>(c, ksteps, acc);
+  }
 }
 
 // Any number of steps (ragged shapes, full tiles only): one activation block
@@ -590,22 +620,34 @@ __device__ __forceinline__ void run_class(const TileCtx& c, int fmw, int ksteps,
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-  if (fmw == 4)
-    run_tile_pp_main<EVEN, WNT, 4, G, LOADS_AFTER>(c, ksteps, acc);
-  else if (fmw == 2)
-    run_tile_pp_main<EVEN, WNT, 2, G, LOADS_AFTER>(c, ksteps, acc);
-  else
-    run_tile_pp_main<EVEN, WNT, 1, G, LOADS_AFTER>(c, ksteps, acc);
+  const bool sh = phase_shifted(ksteps);  // as prologue_class chose for this tile
+  if (fmw == 4) {
+    if (sh) run_tile_pp_main<EVEN, WNT, 4, G, LOADS_AFTER, kShiftSteps>(c, ksteps, acc);
+    else run_tile_pp_main<EVEN, WNT, 4, G, LOADS_AFTER>(c, ksteps, acc);
+  } else if (fmw == 2) {
+    if (sh) run_tile_pp_main<EVEN, WNT, 2, G, LOADS_AFTER, kShiftSteps>(c, ksteps, acc);
+    else run_tile_pp_main<EVEN, WNT, 2, G, LOADS_AFTER>(c, ksteps, acc);
+  } else {
+    if (sh) run_tile_pp_main<EVEN, WNT, 1, G, LOADS_AFTER, kShiftSteps>(c, ksteps, acc);
+    else run_tile_pp_main<EVEN, WNT, 1, G, LOADS_AFTER>(c, ksteps, acc);
+  }
 }
 
+// ksteps: the tile's contraction steps, which choose its schedule (the main
+// loop must be run with the same ksteps).
 template <bool EVEN, bool WNT, int G>
-__device__ __forceinline__ void prologue_class(const TileCtx& c, int fmw) {
-  if (fmw == 4)
-    pp_prologue<EVEN, WNT, 4, G>(c);
-  else if (fmw == 2)
-    pp_prologue<EVEN, WNT, 2, G>(c);
-  else
-    pp_prologue<EVEN, WNT, 1, G>(c);
+__device__ __forceinline__ void prologue_class(const TileCtx& c, int fmw, int ksteps) {
+  const bool sh = phase_shifted(ksteps);
+  if (fmw == 4) {
+    if (sh) pp_prologue<EVEN, WNT, 4, G, kShiftSteps>(c);
+    else pp_prologue<EVEN, WNT, 4, G>(c);
+  } else if (fmw == 2) {
+    if (sh) pp_prologue<EVEN, WNT, 2, G, kShiftSteps>(c);
+    else pp_prologue<EVEN, WNT, 2, G>(c);
+  } else {
+    if (sh) pp_prologue<EVEN, WNT, 1, G, kShiftSteps>(c);
+    else pp_prologue<EVEN, WNT, 1, G>(c);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -746,7 +788,7 @@ __device__ __forceinline__ void up_tiles(
   int slot[A_DMA];
   load_slots(slot, row0, fmw);
   TileCtx c = make_ctx(nt, e, fmw, slot, kp);
-  if constexpr (EVEN) prologue_class<true, WNT, G>(c, fmw);
+  if constexpr (EVEN) prologue_class<true, WNT, G>(c, fmw, kp < 0 ? ksteps : ksteps / 2);
   for (;;) {
     int mt2 = 0, nt2 = 0, e2 = 0, kp2 = -1;
     const bool more = map_unit(L + gridDim.x, mt2, nt2, e2, kp2);
@@ -768,7 +810,7 @@ __device__ __forceinline__ void up_tiles(
     if (more) {
       c = make_ctx(nt2, e2, fmw2, slot, kp2);
       asm volatile("" ::: "memory");
-      if constexpr (EVEN) prologue_class<true, WNT, G>(c, fmw2);
+      if constexpr (EVEN) prologue_class<true, WNT, G>(c, fmw2, kp2 < 0 ? ksteps : ksteps / 2);
       asm volatile("" ::: "memory");
     }
     if (kp < 0)
