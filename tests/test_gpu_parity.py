@@ -1,7 +1,8 @@
 """GPU parity of every libmoe entry point against the fp64 oracle, at sizes the
 oracle finishes in seconds: several row/column/contraction tiles, ragged
-tails, both expert paths (weight streaming for T <= 32 by default, up to 64
-when forced; matrix-core tiles above), forced skewed and empty-expert routings, K and n variants."""
+tails, both expert paths (weight streaming for T <= 80 by default, up to 128
+when forced; matrix-core tiles above), forced skewed and empty-expert routings, K and n variants,
+and every router kernel (vector, one-launch matrix-core, slice kernel with either selection pass)."""
 import numpy as np
 import pytest
 
