@@ -116,6 +116,12 @@ SHAPES = [
     ("router_t64", 64, 256, 384, 8, 2, 42),
     ("router_t65", 65, 256, 384, 8, 2, 43),
     ("decode_n16_k2", 24, 256, 384, 16, 2, 44),
+    # the tiled products' shifted schedule (contractions of 8 + 12 r steps:
+    # the first 8 as a straight-line head, then r whole rounds): 20 steps in
+    # both products (dim 640; hidden 1280, two halves of 640), and 44 (dim
+    # 1408; hidden 2816, two halves of 1408)
+    ("shift_head_1_round", 300, 640, 1280, 8, 2, 56),
+    ("shift_head_3_rounds", 300, 1408, 2816, 8, 2, 57),
     # one expert with 17 row tiles: cut into blocks of 9 and 8 row tiles in
     # the tiled products' tile order (an expert is cut from 16 row tiles on)
     ("one_expert_17_row_tiles", 4200, 256, 512, 1, 1, 45),
